@@ -1,0 +1,166 @@
+/*
+ * mla_verify.h -- C ABI of the MI355X (gfx950) MLA tree-verify attention library.
+ *
+ * The operation is absorbed-form Multi-head Latent Attention for the verify
+ * step of tree speculative decoding: every draft-tree token's query heads
+ * attend over the shared compressed KV cache plus the tree's own tokens under
+ * an ancestor mask. (Page "The Flash Attention Kernel That Had to Be Built:
+ * Designing sm_120 MLA Verify", sections "Strategic Context" and "What Input
+ * Knowledge Is Required": 512-d latent kv_c plus a 64-d decoupled rope key per
+ * cached token, absorbed q_nope plus q_pe per query head, masked positions set
+ * to -inf before the softmax. Page "The Moment of Truth", benchmark table
+ * header: H=64, Dl=512, Dr=64.)
+ *
+ *   s[i,h,j]  = scale * (q_nope[i,h,:] . kv_latent[j,:] + q_rope[i,h,:] . k_rope[j,:])
+ *   visible   = j < P  or  (j - P) is i itself or an ancestor of i in the tree
+ *   out[i,h]  = softmax_j(s[i,h,visible]) @ kv_latent[visible]     (fp32)
+ *   lse[i,h]  = ln sum_j exp(s[i,h,j])  over the visible keys     (fp32, natural log)
+ *
+ * The KV is split into chunks processed by separate workgroups (flash-decode
+ * partials) and a second kernel merges them with the log-sum-exp combine
+ * (page "The Decisive Microbench", section "The KV-Split Solution").
+ *
+ * Conventions for every entry point below:
+ *  - bf16 tensors are passed as raw 16-bit patterns (const void*), row-major
+ *    and contiguous; fp32 outputs likewise. All tensor pointers are DEVICE
+ *    pointers unless a name says host.
+ *  - KV layout per sequence: rows [0, P) are the cached prefix, rows
+ *    [P, P+q) are the q draft-tree tokens in node order (node t at row P+t).
+ *  - tree_parent[i] is -1 (a child of the last committed prefix token) or an
+ *    earlier node index in [0, i). Each token sees itself and its ancestors.
+ *  - The caller owns every buffer. The library allocates no device memory and
+ *    keeps no pointer after a call returns. Inputs are read only; out and lse
+ *    are fully overwritten. Aliasing between inputs, outputs and workspace is
+ *    undefined behaviour.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream): no host synchronisation, no allocation and no device-to-host
+ *    copy happen inside, so a call can be captured into a HIP graph.
+ *  - Arguments are validated on the host before anything is launched; on an
+ *    error nothing is launched and a status code is returned. The device-side
+ *    contents (the tree, the offsets) are a documented precondition; the
+ *    kernels stay in bounds for any tree (the ancestor walk is bounded by q)
+ *    and write NaN for a sequence whose offsets are inconsistent.
+ *  - Launch failures return MLAV_ERR_HIP; faults inside a kernel surface at the
+ *    caller's next synchronisation.
+ */
+#ifndef MLA_VERIFY_H
+#define MLA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MLAV_OK 0
+#define MLAV_ERR_NULL 1        /* a required pointer is NULL */
+#define MLAV_ERR_SHAPE 2       /* a size is out of range */
+#define MLAV_ERR_TREE 3        /* tree_parent is not topologically ordered (host check) */
+#define MLAV_ERR_ALIGN 4       /* a tensor pointer is not 16-byte aligned (lse and parents: 4) */
+#define MLAV_ERR_WORKSPACE 5   /* workspace missing or smaller than mla_verify_workspace_size */
+#define MLAV_ERR_UNSUPPORTED 6 /* a valid but unimplemented configuration (num_heads != 64) */
+#define MLAV_ERR_HIP 7         /* the HIP runtime reported an error */
+#define MLAV_ERR_ARG 8         /* a scalar or option value is invalid */
+
+#define MLAV_MAX_Q 64    /* q_len limit: one 64-bit ancestor mask per token */
+#define MLAV_HEADS 64    /* the head count the kernels are built for */
+#define MLAV_DL 512      /* latent width (value width) */
+#define MLAV_DR 64       /* rope width */
+
+/* Tuning knobs; a NULL options pointer means all zeros. */
+typedef struct mlav_options {
+  int32_t nsplit;  /* 0: the planner picks the KV split count; >0: request this many
+                      splits (the planner rounds the chunk to whole tiles, so the
+                      effective count can be lower) */
+  int32_t pv_mode; /* 0: softmax weights enter the value product as a bf16 hi+lo
+                      pair (about 16 significant bits, the default);
+                      1: a single bf16 weight (8 bits; faster, looser) */
+  int32_t kernel;  /* 0: bf16 MFMA kernel (default); 1: plain fp32 VALU kernel
+                      (a slow second implementation kept for cross-checks) */
+  int32_t reserved; /* must be 0 */
+} mlav_options;
+
+/* What the planner decided for one call. */
+typedef struct mlav_plan {
+  int32_t nsplit;  /* KV splits per sequence (of the longest sequence) */
+  int32_t tile;    /* keys per wave tile */
+  int64_t chunk;   /* keys per split (a multiple of 2*tile) */
+  int32_t grid;    /* workgroups of the split kernel */
+  int32_t combine; /* 1 when the combine kernel runs (nsplit > 1) */
+} mlav_plan;
+
+/*
+ * One sequence.
+ *   q_nope_absorbed [q_len, num_heads, 512] bf16   absorbed nope query
+ *   q_rope          [q_len, num_heads, 64]  bf16   rope query (RoPE already applied)
+ *   kv_latent       [prefix_len + q_len, 512] bf16 latent keys = values
+ *   k_rope          [prefix_len + q_len, 64]  bf16 rope keys
+ *   tree_parent     [q_len] int32
+ *   prefix_len      >= 0 cached tokens before the tree
+ *   scale           fp32 factor on the whole 576-d dot product
+ *   out             [q_len, num_heads, 512] fp32
+ *   lse             [q_len, num_heads] fp32, natural log
+ *   q_len           1 .. 64;  num_heads must be 64
+ *   workspace       device scratch of at least mla_verify_workspace_size(...)
+ *                   bytes (may be NULL when that size is 0)
+ */
+int32_t mla_verify(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                   const void* k_rope, const int32_t* tree_parent, int64_t prefix_len, float scale,
+                   float* out, float* lse, int32_t q_len, int32_t num_heads, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* mla_verify with explicit options (NULL = defaults). */
+int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                      const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
+                      float scale, float* out, float* lse, int32_t q_len, int32_t num_heads,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      const mlav_options* opt);
+
+/*
+ * batch independent sequences sharing q_len; sequence b owns KV rows
+ * [kv_offsets[b], kv_offsets[b+1]) (its prefix then its q_len tree tokens).
+ *   q_nope_absorbed [batch, q_len, num_heads, 512], q_rope [batch, q_len, num_heads, 64]
+ *   kv_latent [total_kv, 512], k_rope [total_kv, 64], tree_parent [batch, q_len]
+ *   kv_offsets [batch + 1] int64 DEVICE array, kv_offsets[0] = 0
+ *   total_kv = kv_offsets[batch], max_kv = max_b (kv_offsets[b+1] - kv_offsets[b]):
+ *   host copies of two device facts, used for planning and bounds checks
+ *   out [batch, q_len, num_heads, 512], lse [batch, q_len, num_heads]
+ */
+int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                           const void* k_rope, const int32_t* tree_parent,
+                           const int64_t* kv_offsets, int32_t batch, int64_t total_kv,
+                           int64_t max_kv, float scale, float* out, float* lse, int32_t q_len,
+                           int32_t num_heads, void* workspace, size_t workspace_bytes,
+                           void* stream, const mlav_options* opt);
+
+/* Workspace bytes a call with these sizes needs (0 when no split is needed).
+   num_cus = 0 queries the current HIP device; pass the CU count to plan
+   without a device. For one sequence use batch = 1 and
+   total_kv = max_kv = prefix_len + q_len. Returns 0 for invalid sizes. */
+size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
+                                 int64_t max_kv, int32_t num_cus, const mlav_options* opt);
+
+/* The planner as a pure host function (no HIP call). */
+int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
+                        int64_t max_kv, int32_t num_cus, const mlav_options* opt,
+                        mlav_plan* plan_out);
+
+/* Host-side check of a HOST copy of a tree: MLAV_OK or MLAV_ERR_TREE. */
+int32_t mla_verify_check_tree(const int32_t* host_parent, int32_t q_len);
+
+/* The combine kernel alone, on caller-made partials:
+   part_out [nsplit, rows, 512] fp32 (each normalised), part_lse [nsplit, rows]
+   fp32 (natural log; -inf marks an empty part) -> out [rows, 512], lse [rows]. */
+int32_t mla_verify_combine(const float* part_out, const float* part_lse, int32_t nsplit,
+                           int64_t rows, float* out, float* lse, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* mla_verify_strerror(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_VERIFY_H */

@@ -1,0 +1,146 @@
+"""torch-facing wrappers of the C ABI (device memory and streams come from torch).
+
+    out, lse = mla_verify(q_nope, q_rope, kv_latent, k_rope, tree_parent, prefix_len, scale)
+
+Inputs are bf16 CUDA (HIP) tensors, row-major and contiguous; tree_parent is
+int32 on the same device. Outputs are fp32. The work runs on the current torch
+stream; the call returns without synchronising.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+H = 64
+DL = 512
+DR = 64
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def mla_verify(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tensor, k_rope: torch.Tensor,
+               tree_parent: torch.Tensor, prefix_len: int, scale: float,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, nsplit: int = 0, pv_mode: int = 0,
+               kernel: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One sequence: q_nope [q,H,512], q_rope [q,H,64], kv_latent [P+q,512], k_rope [P+q,64]
+    (bf16), tree_parent [q] int32 -> out [q,H,512] fp32, lse [q,H] fp32."""
+    if not q_nope.is_cuda:
+        raise ValueError("inputs must be on a GPU (the library has no CPU path)")
+    dev = q_nope.device
+    q, h = int(q_nope.shape[0]), int(q_nope.shape[1])
+    n = int(prefix_len) + q
+    _check(q_nope, "q_nope", torch.bfloat16, (q, h, DL), dev)
+    _check(q_rope, "q_rope", torch.bfloat16, (q, h, DR), dev)
+    _check(kv_latent, "kv_latent", torch.bfloat16, (n, DL), dev)
+    _check(k_rope, "k_rope", torch.bfloat16, (n, DR), dev)
+    _check(tree_parent, "tree_parent", torch.int32, (q,), dev)
+    if out is None:
+        out = torch.empty(q, h, DL, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(q, h, dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, (q, h, DL), dev)
+    _check(lse, "lse", torch.float32, (q, h), dev)
+    lib = _lib.load()
+    opt = _lib.options(nsplit, pv_mode, kernel)
+    need = int(lib.mla_verify_workspace_size(q, h, 1, n, n, 0, ctypes.byref(opt)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.mla_verify_ex(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(), k_rope.data_ptr(),
+                           tree_parent.data_ptr(), int(prefix_len), float(scale), out.data_ptr(),
+                           lse.data_ptr(), q, h, ws_ptr, ws_bytes, _stream_ptr(dev), ctypes.byref(opt))
+    if rc != _lib.MLAV_OK:
+        raise _lib.MLAVError(rc, "mla_verify")
+    return out, lse
+
+
+def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tensor,
+                       k_rope: torch.Tensor, tree_parent: torch.Tensor, kv_offsets: torch.Tensor,
+                       scale: float, max_kv: Optional[int] = None,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, nsplit: int = 0, pv_mode: int = 0,
+                       kernel: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """B sequences: q_nope [B,q,H,512], kv rows of sequence b = [off[b], off[b+1]),
+    tree_parent [B,q] int32, kv_offsets [B+1] int64 (CPU or device)."""
+    if not q_nope.is_cuda:
+        raise ValueError("inputs must be on a GPU (the library has no CPU path)")
+    dev = q_nope.device
+    bsz, q, h = int(q_nope.shape[0]), int(q_nope.shape[1]), int(q_nope.shape[2])
+    total = int(kv_latent.shape[0])
+    if kv_offsets.dtype != torch.int64 or tuple(kv_offsets.shape) != (bsz + 1,):
+        raise ValueError("kv_offsets must be int64 [B+1]")
+    if max_kv is None or not kv_offsets.is_cuda:
+        host = kv_offsets.detach().cpu()
+        max_kv = int((host[1:] - host[:-1]).max().item()) if max_kv is None else int(max_kv)
+    offs_dev = kv_offsets.to(dev) if not kv_offsets.is_cuda else kv_offsets
+    _check(q_nope, "q_nope", torch.bfloat16, (bsz, q, h, DL), dev)
+    _check(q_rope, "q_rope", torch.bfloat16, (bsz, q, h, DR), dev)
+    _check(kv_latent, "kv_latent", torch.bfloat16, (total, DL), dev)
+    _check(k_rope, "k_rope", torch.bfloat16, (total, DR), dev)
+    _check(tree_parent, "tree_parent", torch.int32, (bsz, q), dev)
+    if out is None:
+        out = torch.empty(bsz, q, h, DL, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(bsz, q, h, dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, (bsz, q, h, DL), dev)
+    _check(lse, "lse", torch.float32, (bsz, q, h), dev)
+    lib = _lib.load()
+    opt = _lib.options(nsplit, pv_mode, kernel)
+    need = int(lib.mla_verify_workspace_size(q, h, bsz, total, max_kv, 0, ctypes.byref(opt)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.mla_verify_batched(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(), k_rope.data_ptr(),
+                                tree_parent.data_ptr(), offs_dev.data_ptr(), bsz, total, max_kv,
+                                float(scale), out.data_ptr(), lse.data_ptr(), q, h, ws_ptr, ws_bytes,
+                                _stream_ptr(dev), ctypes.byref(opt))
+    if rc != _lib.MLAV_OK:
+        raise _lib.MLAVError(rc, "mla_verify_batched")
+    return out, lse
+
+
+def combine(part_out: torch.Tensor, part_lse: torch.Tensor,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """LSE merge of caller-made partials: part_out [S, rows, 512], part_lse [S, rows]."""
+    dev = part_out.device
+    s, rows = int(part_out.shape[0]), int(part_out.shape[1])
+    _check(part_out, "part_out", torch.float32, (s, rows, DL), dev)
+    _check(part_lse, "part_lse", torch.float32, (s, rows), dev)
+    if out is None:
+        out = torch.empty(rows, DL, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    rc = _lib.load().mla_verify_combine(part_out.data_ptr(), part_lse.data_ptr(), s, rows, out.data_ptr(),
+                                        lse.data_ptr(), _stream_ptr(dev))
+    if rc != _lib.MLAV_OK:
+        raise _lib.MLAVError(rc, "mla_verify_combine")
+    return out, lse
+
+
+def device_plan(q_len: int, batch: int, total_kv: int, max_kv: int, nsplit: int = 0, pv_mode: int = 0,
+                kernel: int = 0, device=None) -> _lib.Plan:
+    """The plan a call on `device` would use (reads the device's CU count)."""
+    props = torch.cuda.get_device_properties(device if device is not None else torch.cuda.current_device())
+    return _lib.plan(q_len, H, batch, total_kv, max_kv, props.multi_processor_count, nsplit, pv_mode, kernel)

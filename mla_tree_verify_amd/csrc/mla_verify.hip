@@ -1,0 +1,813 @@
+// MLA tree-verify attention for MI355X (gfx950): kernels and the C ABI.
+//
+// What is computed is stated in include/mla_verify.h. The method follows the
+// pages' flash-decode design (page "The Decisive Microbench", section "The
+// KV-Split Solution": each workgroup attends over one contiguous KV slice,
+// writes its partial result with its log-sum-exp, and a light second kernel
+// merges the slices) and their tile reuse across heads (page "The Flash
+// Attention Kernel That Had to Be Built", section "The Final Architecture":
+// one KV tile in shared memory serves several heads). The execution layout is
+// designed for CDNA4 rather than taken from the pages' sm_120 kernels:
+//
+//  * One workgroup = one draft token x all 64 heads x one KV chunk. Because the
+//    latent KV is shared by every head, scores and values are dense
+//    contractions: S^T[keys x heads] = K[keys x 576] Q^T and
+//    O^T[dims x heads] += V^T[dims x keys] P^T, both on bf16 MFMA 32x32x16
+//    with fp32 accumulation.
+//  * 4 waves = 2 head halves x 2 dim halves. A wave keeps the queries of its
+//    32 heads over its half of the 576 dims in registers (72 VGPRs) and
+//    computes partial scores for every 32-key tile; the two waves of a head
+//    half swap partials through LDS, so both hold the same full scores, the
+//    same softmax weights and denominators. Each then accumulates 256 of the
+//    512 output dims (128 AGPRs). Every wave reads a tile's K and V once, so a
+//    CU does about 32 MFMA flops per LDS byte.
+//  * KV tiles go from HBM straight into LDS with 16-byte buffer loads
+//    (buffer_load_dwordx4 ... lds) into a 3-slot ring; loads past the sequence
+//    end return zeros. 16-byte chunks are XOR swizzled per key so that the
+//    128-bit score-operand reads and the transposing value-operand reads
+//    (ds_read_b64_tr_b16) avoid bank conflicts.
+//  * The S^T accumulator layout equals the P^T operand layout of the value
+//    product, so softmax weights never leave registers. Row max and sum need a
+//    single cross-lane step (v_permlane32_swap). The next tile's score MFMAs
+//    are issued before this tile's softmax so the two overlap.
+//  * The softmax reference max is fixed by the first visible tile and never
+//    moves, so the accumulator is never rescaled inside the loop (a chunk
+//    whose scores climb more than 2^64 above it is redone once with the
+//    chunk's own max).
+//  * Softmax weights enter the value product as a bf16 hi+lo pair (two MFMAs
+//    sharing the V operand), about 16 significant bits; a single bf16 weight
+//    is an option.
+//  * Workgroup ids are mapped so that all tokens of one KV chunk run on the
+//    same XCD (ids are dealt round-robin over the 8 XCDs), and the chunk is
+//    read from HBM once into that XCD's L2.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "mla_verify.h"
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace mlav {
+
+constexpr int kHeads = MLAV_HEADS;
+constexpr int kDl = MLAV_DL;
+constexpr int kDr = MLAV_DR;
+constexpr int kTile = 32;                        // keys per wave tile
+constexpr int kLatBytes = kTile * kDl * 2;       // 32768
+constexpr int kRopeBytes = kTile * kDr * 2;      // 4096
+constexpr int kTileBytes = kLatBytes + kRopeBytes;  // 36864
+constexpr int kRing = 3;                         // tiles in flight
+constexpr int kLdsBytes = kRing * kTileBytes + 2 * 4 * 16 * 64 * 4;  // + score exchange = 143360
+constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+constexpr int64_t kChunkGran = kTile;
+constexpr int64_t kMinChunk = 128;
+constexpr float kRefHeadroom = 64.0f;  // log2 units: weights stay below 2^64
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct Args {
+  const uint16_t* qn;    // [B, q, H, 512]
+  const uint16_t* qr;    // [B, q, H, 64]
+  const uint16_t* lat;   // [total, 512]
+  const uint16_t* rope;  // [total, 64]
+  const int32_t* parent; // [B, q]
+  const int64_t* offs;   // [B + 1] or null (one sequence of single_n rows)
+  float* out;            // [B, q, H, 512]
+  float* lse;            // [B, q, H]
+  float* part_o;         // [B, S, q, H, 512]
+  float* part_lse;       // [B, S, q, H]
+  int64_t single_n;
+  int64_t total_kv;
+  int64_t max_kv;
+  int64_t chunk;
+  float scale_log2;
+  int32_t q;
+  int32_t batch;
+  int32_t nsplit;
+  int32_t nwork;
+  int32_t per_xcd;
+  int32_t fixed_ns;      // combine only: >0 forces every row's split count
+};
+
+// ---------------------------------------------------------------------------
+// shared device helpers
+// ---------------------------------------------------------------------------
+__device__ inline bool seq_bounds(const Args& a, int b, int64_t& row0, int64_t& n) {
+  if (a.offs == nullptr) {
+    row0 = 0;
+    n = a.single_n;
+    return true;
+  }
+  row0 = a.offs[b];
+  const int64_t r1 = a.offs[b + 1];
+  n = r1 - row0;
+  return row0 >= 0 && r1 <= a.total_kv && n >= a.q && n <= a.max_kv;
+}
+
+// Ancestor-or-self mask of draft token t (bit u set = tree node u visible).
+// The walk is bounded by q steps and by the index range, whatever the tree.
+__device__ inline uint64_t ancestor_mask(const int32_t* parent, int q, int t) {
+  uint64_t anc = 0;
+  int node = t;
+  for (int step = 0; step < q && node >= 0 && node < q; ++step) {
+    anc |= 1ull << node;
+    node = parent[node];
+  }
+  return anc;
+}
+
+__device__ inline bool key_visible(int64_t j, int64_t c1, int64_t prefix, uint64_t anc) {
+  return j < c1 && (j < prefix || ((anc >> (j - prefix)) & 1ull));
+}
+
+// Logical <-> physical 16-byte chunk swizzle inside a key row (low 3 bits only).
+__device__ inline int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
+
+__device__ inline float fmax3(float a, float b) { return a > b ? a : b; }
+
+__device__ inline float partner_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax3(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float partner_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Work id -> (sequence, split, token); tokens of one chunk are consecutive ids.
+// Values are made wave-uniform explicitly so that addresses built from them
+// stay in scalar registers.
+__device__ inline bool decode_work(const Args& a, int& b, int& s, int& t) {
+  const int bid = blockIdx.x;
+  const int w = uniform((bid % kXcds) * a.per_xcd + bid / kXcds);
+  if (w >= a.nwork) return false;
+  t = uniform(w % a.q);
+  const int bs = uniform(w / a.q);
+  s = uniform(bs % a.nsplit);
+  b = uniform(bs / a.nsplit);
+  return true;
+}
+
+__device__ inline void write_nan_token(const Args& a, int b, int t, int tid, int nthreads) {
+  const float nan = __builtin_nanf("");
+  float* o = a.out + ((int64_t)b * a.q + t) * kHeads * kDl;
+  for (int i = tid; i < kHeads * kDl; i += nthreads) o[i] = nan;
+  for (int i = tid; i < kHeads; i += nthreads) a.lse[((int64_t)b * a.q + t) * kHeads + i] = nan;
+}
+
+// ---------------------------------------------------------------------------
+// split kernel: bf16 MFMA
+// ---------------------------------------------------------------------------
+// Buffer descriptor over `bytes` bytes at `base` (gfx9 raw buffer, stride 0):
+// loads past `bytes` return zeros, which zero-fills tiles past the sequence end.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Issue this wave's quarter of the direct-to-LDS loads of one 32-key tile.
+// key_rel = first key of the tile relative to the descriptors' first row.
+// Latent row k lands at buf + 1024 k with its 16-byte chunks XOR-swizzled by
+// swz(k); the rope rows follow the 32 latent rows, 128 B each, swizzled alike.
+__device__ inline void issue_tile(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_rs,
+                                  __amdgpu_buffer_rsrc_t rope_rs, int key_rel, int wave, int lane,
+                                  int rope_voff) {
+  // The whole byte offset goes in the VGPR operand: raw-buffer range checks
+  // cover the VGPR offset (plus the immediate) but not the SGPR offset.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = 4 * i + wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rs, (LDS_AS void*)(buf + k * 1024), 16,
+                                             (key_rel + k) * 1024 + 16 * (lane ^ swz(k)), 0, 0, 0);
+  }
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rs, (LDS_AS void*)(buf + kLatBytes + wave * 1024), 16,
+                                           (key_rel + 8 * wave) * 128 + rope_voff, 0, 0, 0);
+}
+
+// Partial scores of one tile over this wave's half of the 576 dims:
+// S^T[32 keys x 32 heads] = K[32 keys x 288] Q^T[288 x 32 heads].
+// Lane layout (A operand): key lane&31, dims 16 ks + 8 (lane>>5) of the half.
+template <int kDh>
+__device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&qreg)[18], int key,
+                                       int half) {
+  f32x16_t sc = {};
+  const int sw = swz(key);
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    const int c = 36 * kDh + 2 * ks + half;  // logical 16-byte chunk of the 576-d row
+    int off;
+    if (36 * kDh + 2 * ks < 64)
+      off = key * 1024 + 16 * ((c & ~7) | ((c & 7) ^ sw));
+    else
+      off = kLatBytes + key * 128 + 16 * ((c - 64) ^ sw);
+    const bf16x8_t kv = *(const LDS_AS bf16x8_t*)(buf + off);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[ks], sc, 0, 0, 0);
+  }
+  return sc;
+}
+
+// Values of one tile for this wave's 256 output dims:
+// O^T[256 dims x 32 heads] += V^T[256 x 32 keys] P^T[32 keys x 32 heads].
+// V^T comes from the latent rows through transposing LDS reads.
+template <int kDh, bool kHiLo>
+__device__ inline void tile_values(f32x16_t (&acc)[8], const LDS_AS char* buf, int pv_off_even,
+                                   int pv_off_odd, const bf16x8_t (&p_hi)[2],
+                                   const bf16x8_t (&p_lo)[2]) {
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      constexpr int kDb0 = 8 * kDh;
+      const int dbg = kDb0 + db;
+      const int base = ((dbg & 1) ? pv_off_odd : pv_off_even) + 128 * (dbg >> 1) + 16 * 1024 * ks2;
+      const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(buf + base));
+      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(buf + base + 8 * 1024));
+      const bf16x8_t vt = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, p_hi[ks2], acc[db], 0, 0, 0);
+      if (kHiLo) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, p_lo[ks2], acc[db], 0, 0, 0);
+    }
+  }
+}
+
+// One workgroup = one draft token x 64 heads x one KV chunk; 4 waves =
+// 2 head halves (hh) x 2 dim halves (kDh). Both waves of a head half compute
+// partial scores over their dim half, swap them through LDS and end up with
+// identical full scores, softmax weights and denominators; each then owns
+// 256 of the 512 output dims.
+template <int kDh, bool kHiLo>
+__device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s, int t, int wave,
+                                  int hh, int lane, int64_t row0, int64_t n) {
+  const int half = lane >> 5;
+  const int64_t prefix = n - a.q;
+  const int64_t c0 = (int64_t)s * a.chunk;
+  const int64_t c1 = c0 + a.chunk < n ? c0 + a.chunk : n;
+  const int nsplit_b = (int)((n + a.chunk - 1) / a.chunk);
+  const uint64_t anc = ancestor_mask(a.parent + (int64_t)b * a.q, a.q, t);
+  const int head = 32 * hh + (lane & 31);
+
+  // resident queries for this wave's dim half: B operand of S^T = K Q^T
+  bf16x8_t qreg[18];
+  {
+    const int64_t qrow = ((int64_t)b * a.q + t) * kHeads + head;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const int d = 288 * kDh + 16 * ks + 8 * half;
+      qreg[ks] = d < kDl ? *(const bf16x8_t*)(a.qn + qrow * kDl + d)
+                         : *(const bf16x8_t*)(a.qr + qrow * kDr + (d - kDl));
+    }
+  }
+
+  int pv_off_even, pv_off_odd;
+  {
+    const int i = lane & 15;
+    const int dhalf = (lane >> 4) & 1;
+    const int kk = 4 * half + (i >> 2);
+    const int z = (2 * dhalf + ((i & 3) >> 1)) ^ (((i >> 2) << 1) | half);
+    pv_off_even = kk * 1024 + 16 * z + 8 * (i & 1);
+    pv_off_odd = kk * 1024 + 16 * (z ^ 4) + 8 * (i & 1);
+  }
+
+  const int ntiles = (int)((c1 - c0 + kTile - 1) / kTile);
+  const __amdgpu_buffer_rsrc_t lat_rs =
+      make_rsrc(a.lat + (row0 + c0) * kDl, (uint32_t)((n - c0) * kDl * 2));
+  const __amdgpu_buffer_rsrc_t rope_rs =
+      make_rsrc(a.rope + (row0 + c0) * kDr, (uint32_t)((n - c0) * kDr * 2));
+  const int rope_voff = (lane >> 3) * 128 + 16 * ((lane & 7) ^ swz(lane >> 3));
+
+  LDS_AS float* xs = (LDS_AS float*)(lds + kRing * kTileBytes);  // [2][4 waves][16][64]
+  const int partner = wave ^ 1;  // same head half, other dim half
+  const int key = lane & 31;
+
+  // Online softmax with a reference max that never moves inside the loop: the
+  // first visible tile fixes it, later weights are 2^(s - m_ref), exact for
+  // any m_ref. A score more than kRefHeadroom above m_ref could overflow; then
+  // the chunk is redone once with m_ref = the chunk's observed max, which no
+  // score exceeds. The accumulator is never rescaled inside the loop.
+  f32x16_t acc[8];
+  float m_ref = -INFINITY;  // log2 units, this lane's head
+  float l_run = 0.f;        // this lane's share of the softmax denominator
+  float m_seen = -INFINITY;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = (f32x16_t){};
+    l_run = 0.f;
+    if (attempt == 1) m_ref = m_seen;
+    int ovf = 0;
+
+    // prologue: tiles 0 and 1 in flight, partial scores of tile 0 published
+    issue_tile(lds, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+    if (ntiles > 1) issue_tile(lds + kTileBytes, lat_rs, rope_rs, kTile, wave, lane, rope_voff);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    f32x16_t own = tile_scores<kDh>(lds, qreg, key, half);
+    {
+      LDS_AS float* dst = xs + (0 * 4 + wave) * 1024;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = own[r];
+    }
+
+    for (int i = 0; i < ntiles; ++i) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // tile i+1 landed (this wave's part)
+      __syncthreads();  // all parts landed; partial scores of tile i published; slot (i+2)%3 free
+      if (i + 2 < ntiles)
+        issue_tile(lds + ((i + 2) % kRing) * kTileBytes, lat_rs, rope_rs, (i + 2) * kTile, wave,
+                   lane, rope_voff);
+      // next tile's score MFMAs go first so that they overlap this tile's softmax
+      f32x16_t nxt;
+      if (i + 1 < ntiles) nxt = tile_scores<kDh>(lds + ((i + 1) % kRing) * kTileBytes, qreg, key, half);
+
+      const LDS_AS float* src = xs + ((i & 1) * 4 + partner) * 1024;
+      const int64_t key0 = c0 + (int64_t)i * kTile;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (own[r] + src[r * 64 + lane]) * a.scale_log2;
+      if (key0 + kTile > prefix || key0 + kTile > c1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t j = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (!key_visible(j, c1, prefix, anc)) x[r] = -INFINITY;
+        }
+      }
+      float mt = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmax3(mt, x[r]);
+      mt = partner_max(mt);
+      m_seen = fmax3(m_seen, mt);
+      if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated for this head yet
+      ovf |= mt > m_ref + kRefHeadroom;
+      const float mref = m_ref == -INFINITY ? 0.f : m_ref;
+
+      // softmax weights straight into the P^T operand layout
+      bf16x8_t p_hi[2], p_lo[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pw = __builtin_amdgcn_exp2f(x[r] - mref);
+        l_run += pw;
+        const __bf16 h = (__bf16)pw;
+        p_hi[r >> 3][r & 7] = h;
+        p_lo[r >> 3][r & 7] = kHiLo ? (__bf16)(pw - (float)h) : (__bf16)0.f;
+      }
+      tile_values<kDh, kHiLo>(acc, lds + (i % kRing) * kTileBytes, pv_off_even, pv_off_odd, p_hi, p_lo);
+
+      if (i + 1 < ntiles) {
+        LDS_AS float* dst = xs + (((i + 1) & 1) * 4 + wave) * 1024;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = nxt[r];
+        own = nxt;
+      }
+    }
+    if (!__syncthreads_or(ovf)) break;
+    __syncthreads();
+  }
+
+  // normalise and store this wave's 32 heads x 256 dims
+  const float l_tot = partner_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_val = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  const bool final_write = nsplit_b == 1;
+  const int64_t qrow = ((int64_t)b * a.q + t) * kHeads + head;
+  float* orow = final_write
+                    ? a.out + qrow * kDl
+                    : a.part_o + ((((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head) * kDl;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t v;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = acc[db][4 * g + c] * inv;
+      *(f32x4_t*)(orow + 256 * kDh + 32 * db + 8 * g + 4 * half) = v;
+    }
+  }
+  if (kDh == 0 && half == 0) {
+    if (final_write)
+      a.lse[qrow] = lse_val;
+    else
+      a.part_lse[(((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head] = lse_val;
+  }
+}
+
+template <bool kHiLo>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void split_mfma_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[kLdsBytes];
+  LDS_AS char* lds = (LDS_AS char*)lds_raw;
+  int b, s, t;
+  if (!decode_work(a, b, s, t)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  int64_t row0, n;
+  if (!seq_bounds(a, b, row0, n)) {
+    if (s == 0) write_nan_token(a, b, t, tid, kThreads);
+    return;
+  }
+  row0 = uniform64(row0);
+  n = uniform64(n);
+  if ((int64_t)s * a.chunk >= n) return;  // this sequence needs fewer splits
+  const int hh = wave >> 1;
+  if ((wave & 1) == 0)
+    split_body<0, kHiLo>(a, lds, b, s, t, wave, hh, lane, row0, n);
+  else
+    split_body<1, kHiLo>(a, lds, b, s, t, wave, hh, lane, row0, n);
+}
+
+// ---------------------------------------------------------------------------
+// split kernel: plain fp32 VALU (second implementation, for cross-checks)
+// one wave per (token, head, split); keys processed one at a time
+// ---------------------------------------------------------------------------
+__device__ inline float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+__global__ __launch_bounds__(kThreads) void split_valu_kernel(Args a) {
+  const int work = blockIdx.x >> 4;  // 16 workgroups x 4 waves = 64 heads per work item
+  const int head = ((blockIdx.x & 15) << 2) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (work >= a.nwork) return;
+  const int t = work % a.q;
+  const int s = (work / a.q) % a.nsplit;
+  const int b = work / (a.q * a.nsplit);
+  int64_t row0, n;
+  if (!seq_bounds(a, b, row0, n)) {
+    if (s == 0 && (blockIdx.x & 15) == 0) write_nan_token(a, b, t, threadIdx.x, kThreads);
+    return;
+  }
+  const int64_t prefix = n - a.q;
+  const int64_t c0 = (int64_t)s * a.chunk;
+  if (c0 >= n) return;
+  const int64_t c1 = c0 + a.chunk < n ? c0 + a.chunk : n;
+  const int nsplit_b = (int)((n + a.chunk - 1) / a.chunk);
+  const uint64_t anc = ancestor_mask(a.parent + (int64_t)b * a.q, a.q, t);
+  const int64_t qrow = ((int64_t)b * a.q + t) * kHeads + head;
+
+  // lane owns query dims [8 lane, 8 lane + 8) of the latent part and dim `lane` of the rope part
+  float qv[9];
+  for (int d = 0; d < 8; ++d) qv[d] = bf16_to_f32(a.qn[qrow * kDl + 8 * lane + d]);
+  qv[8] = bf16_to_f32(a.qr[qrow * kDr + lane]);
+  float m = -INFINITY, l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t j = c0; j < c1; ++j) {
+    if (!key_visible(j, c1, prefix, anc)) continue;
+    const uint16_t* kl = a.lat + (row0 + j) * kDl + 8 * lane;
+    float v[8];
+    float part = 0.f;
+    for (int d = 0; d < 8; ++d) {
+      v[d] = bf16_to_f32(kl[d]);
+      part += qv[d] * v[d];
+    }
+    part += qv[8] * bf16_to_f32(a.rope[(row0 + j) * kDr + lane]);
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+    const float sj = part * a.scale_log2;
+    const float m_new = fmax3(m, sj);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float p = __builtin_amdgcn_exp2f(sj - m_new);
+    l = l * alpha + p;
+    for (int d = 0; d < 8; ++d) acc[d] = acc[d] * alpha + p * v[d];
+    m = m_new;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse_val = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  const bool final_write = nsplit_b == 1;
+  float* orow = final_write
+                    ? a.out + qrow * kDl
+                    : a.part_o + ((((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head) * kDl;
+  for (int d = 0; d < 8; ++d) orow[8 * lane + d] = acc[d] * inv;
+  if (lane == 0) {
+    if (final_write)
+      a.lse[qrow] = lse_val;
+    else
+      a.part_lse[(((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head] = lse_val;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine: log-sum-exp merge of the split partials, 128 threads per row
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  if (row >= rows) return;
+  const int d4 = threadIdx.x & 127;
+  const int64_t rows_b = (int64_t)a.q * kHeads;
+  const int b = (int)(row / rows_b);
+  const int64_t rb = row - (int64_t)b * rows_b;
+  int ns = a.fixed_ns;
+  if (ns <= 0) {
+    int64_t row0, n;
+    if (!seq_bounds(a, b, row0, n)) {
+      const float nan = __builtin_nanf("");
+      *(f32x4_t*)(a.out + row * kDl + 4 * d4) = (f32x4_t){nan, nan, nan, nan};
+      if (d4 == 0) a.lse[row] = nan;
+      return;
+    }
+    ns = (int)((n + a.chunk - 1) / a.chunk);
+    if (ns <= 1) return;  // the split kernel wrote this row directly
+  }
+  const float* pl = a.part_lse + (int64_t)b * a.nsplit * rows_b + rb;
+  const float* po = a.part_o + ((int64_t)b * a.nsplit * rows_b + rb) * kDl + 4 * d4;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmax3(M, pl[s * rows_b]);
+  f32x4_t accv = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < ns; ++s) {
+      const float w = __builtin_amdgcn_exp2f((pl[s * rows_b] - M) * kLog2e);
+      wsum += w;
+      const f32x4_t o = *(const f32x4_t*)(po + s * rows_b * kDl);
+      accv += w * o;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  *(f32x4_t*)(a.out + row * kDl + 4 * d4) = accv * inv;
+  if (d4 == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+int device_cus(int32_t* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLAV_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return MLAV_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return MLAV_ERR_HIP;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return MLAV_OK;
+}
+
+int check_options(const mlav_options* opt) {
+  if (!opt) return MLAV_OK;
+  if (opt->nsplit < 0 || opt->pv_mode < 0 || opt->pv_mode > 1 || opt->kernel < 0 ||
+      opt->kernel > 1 || opt->reserved != 0)
+    return MLAV_ERR_ARG;
+  return MLAV_OK;
+}
+
+int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t max_kv,
+              int32_t num_cus, const mlav_options* opt, mlav_plan* p) {
+  if (q < 1 || q > MLAV_MAX_Q || batch < 1 || heads < 1) return MLAV_ERR_SHAPE;
+  if (heads != kHeads) return MLAV_ERR_UNSUPPORTED;
+  if (max_kv < q || total_kv < (int64_t)batch * q || max_kv > total_kv) return MLAV_ERR_SHAPE;
+  if (max_kv > (int64_t(1) << 40)) return MLAV_ERR_SHAPE;
+  if (num_cus < 1) return MLAV_ERR_ARG;
+  const int rc = check_options(opt);
+  if (rc != MLAV_OK) return rc;
+  const int64_t tokens = (int64_t)batch * q;
+  int64_t chunk;
+  if (opt && opt->nsplit > 0) {
+    chunk = (max_kv + opt->nsplit - 1) / opt->nsplit;
+    chunk = (chunk + kChunkGran - 1) / kChunkGran * kChunkGran;
+  } else {
+    // one resident workgroup per CU: aim for about num_cus workgroups in total
+    int64_t s_avg = num_cus / tokens;
+    if (s_avg < 1) s_avg = 1;
+    const int64_t avg_kv = (total_kv + batch - 1) / batch;
+    chunk = (avg_kv + s_avg - 1) / s_avg;
+    chunk = (chunk + kChunkGran - 1) / kChunkGran * kChunkGran;
+    if (chunk < kMinChunk) chunk = kMinChunk;
+  }
+  const int64_t ns = (max_kv + chunk - 1) / chunk;
+  const int64_t nwork = tokens * ns;
+  if (nwork > (int64_t(1) << 30)) return MLAV_ERR_SHAPE;
+  p->nsplit = (int32_t)ns;
+  p->tile = kTile;
+  p->chunk = chunk;
+  const int kernel = opt ? opt->kernel : 0;
+  if (kernel == 0) {
+    const int64_t per_xcd = (nwork + kXcds - 1) / kXcds;
+    p->grid = (int32_t)(per_xcd * kXcds);
+  } else {
+    p->grid = (int32_t)(nwork * 16);
+  }
+  p->combine = ns > 1 ? 1 : 0;
+  return MLAV_OK;
+}
+
+size_t workspace_bytes_for(const mlav_plan& p, int32_t q, int32_t batch) {
+  if (!p.combine) return 0;
+  return (size_t)batch * p.nsplit * q * kHeads * (kDl + 1) * sizeof(float);
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  Args a = base;
+  a.nsplit = p.nsplit;
+  a.chunk = p.chunk;
+  a.nwork = a.batch * a.q * p.nsplit;
+  a.per_xcd = (a.nwork + kXcds - 1) / kXcds;
+  a.fixed_ns = 0;
+  const int kernel = opt ? opt->kernel : 0;
+  const int pv_mode = opt ? opt->pv_mode : 0;
+  if (kernel == 0) {
+    if (pv_mode == 0)
+      hipLaunchKernelGGL(split_mfma_kernel<true>, dim3(p.grid), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(split_mfma_kernel<false>, dim3(p.grid), dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(split_valu_kernel, dim3(p.grid), dim3(kThreads), 0, st, a);
+  }
+  if (hipGetLastError() != hipSuccess) return MLAV_ERR_HIP;
+  if (p.combine) {
+    const int64_t rows = (int64_t)a.batch * a.q * kHeads;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
+    if (hipGetLastError() != hipSuccess) return MLAV_ERR_HIP;
+  }
+  return MLAV_OK;
+}
+
+int common_checks(const void* qn, const void* qr, const void* lat, const void* rope,
+                  const int32_t* parent, float scale, const float* out, const float* lse,
+                  int32_t q, int32_t heads, const mlav_options* opt) {
+  if (!qn || !qr || !lat || !rope || !parent || !out || !lse) return MLAV_ERR_NULL;
+  if (q < 1 || q > MLAV_MAX_Q || heads < 1) return MLAV_ERR_SHAPE;
+  if (heads != kHeads) return MLAV_ERR_UNSUPPORTED;
+  if (!aligned(qn, 16) || !aligned(qr, 16) || !aligned(lat, 16) || !aligned(rope, 16) ||
+      !aligned(out, 16) || !aligned(lse, 4) || !aligned(parent, 4))
+    return MLAV_ERR_ALIGN;
+  if (!std::isfinite(scale)) return MLAV_ERR_ARG;
+  return check_options(opt);
+}
+
+}  // namespace mlav
+
+using namespace mlav;
+
+extern "C" {
+
+int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
+                        int64_t max_kv, int32_t num_cus, const mlav_options* opt,
+                        mlav_plan* plan_out) {
+  if (!plan_out) return MLAV_ERR_NULL;
+  return plan_impl(q_len, num_heads, batch, total_kv, max_kv, num_cus, opt, plan_out);
+}
+
+size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
+                                 int64_t max_kv, int32_t num_cus, const mlav_options* opt) {
+  if (num_cus <= 0 && device_cus(&num_cus) != MLAV_OK) return 0;
+  mlav_plan p;
+  if (plan_impl(q_len, num_heads, batch, total_kv, max_kv, num_cus, opt, &p) != MLAV_OK) return 0;
+  return workspace_bytes_for(p, q_len, batch);
+}
+
+int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                      const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
+                      float scale, float* out, float* lse, int32_t q_len, int32_t num_heads,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      const mlav_options* opt) {
+  int rc = common_checks(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, scale, out, lse,
+                         q_len, num_heads, opt);
+  if (rc != MLAV_OK) return rc;
+  if (prefix_len < 0 || prefix_len > (int64_t(1) << 40)) return MLAV_ERR_SHAPE;
+  const int64_t n = prefix_len + q_len;
+  int32_t cus = 0;
+  rc = device_cus(&cus);
+  if (rc != MLAV_OK) return rc;
+  mlav_plan p;
+  rc = plan_impl(q_len, num_heads, 1, n, n, cus, opt, &p);
+  if (rc != MLAV_OK) return rc;
+  const size_t need = workspace_bytes_for(p, q_len, 1);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
+  Args a{};
+  a.qn = (const uint16_t*)q_nope_absorbed;
+  a.qr = (const uint16_t*)q_rope;
+  a.lat = (const uint16_t*)kv_latent;
+  a.rope = (const uint16_t*)k_rope;
+  a.parent = tree_parent;
+  a.offs = nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = (float*)workspace;
+  a.part_lse = need ? (float*)workspace + (size_t)p.nsplit * q_len * kHeads * kDl : nullptr;
+  a.single_n = n;
+  a.total_kv = n;
+  a.max_kv = n;
+  a.scale_log2 = scale * kLog2e;
+  a.q = q_len;
+  a.batch = 1;
+  return launch(a, p, opt, stream);
+}
+
+int32_t mla_verify(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                   const void* k_rope, const int32_t* tree_parent, int64_t prefix_len, float scale,
+                   float* out, float* lse, int32_t q_len, int32_t num_heads, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return mla_verify_ex(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, prefix_len, scale,
+                       out, lse, q_len, num_heads, workspace, workspace_bytes, stream, nullptr);
+}
+
+int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                           const void* k_rope, const int32_t* tree_parent,
+                           const int64_t* kv_offsets, int32_t batch, int64_t total_kv,
+                           int64_t max_kv, float scale, float* out, float* lse, int32_t q_len,
+                           int32_t num_heads, void* workspace, size_t workspace_bytes,
+                           void* stream, const mlav_options* opt) {
+  int rc = common_checks(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, scale, out, lse,
+                         q_len, num_heads, opt);
+  if (rc != MLAV_OK) return rc;
+  if (!kv_offsets) return MLAV_ERR_NULL;
+  if (!aligned(kv_offsets, 8)) return MLAV_ERR_ALIGN;
+  if (batch < 1 || max_kv < q_len || total_kv < (int64_t)batch * q_len || max_kv > total_kv)
+    return MLAV_ERR_SHAPE;
+  int32_t cus = 0;
+  rc = device_cus(&cus);
+  if (rc != MLAV_OK) return rc;
+  mlav_plan p;
+  rc = plan_impl(q_len, num_heads, batch, total_kv, max_kv, cus, opt, &p);
+  if (rc != MLAV_OK) return rc;
+  const size_t need = workspace_bytes_for(p, q_len, batch);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
+  Args a{};
+  a.qn = (const uint16_t*)q_nope_absorbed;
+  a.qr = (const uint16_t*)q_rope;
+  a.lat = (const uint16_t*)kv_latent;
+  a.rope = (const uint16_t*)k_rope;
+  a.parent = tree_parent;
+  a.offs = kv_offsets;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = (float*)workspace;
+  a.part_lse =
+      need ? (float*)workspace + (size_t)batch * p.nsplit * q_len * kHeads * kDl : nullptr;
+  a.single_n = 0;
+  a.total_kv = total_kv;
+  a.max_kv = max_kv;
+  a.scale_log2 = scale * kLog2e;
+  a.q = q_len;
+  a.batch = batch;
+  return launch(a, p, opt, stream);
+}
+
+int32_t mla_verify_check_tree(const int32_t* host_parent, int32_t q_len) {
+  if (!host_parent) return MLAV_ERR_NULL;
+  if (q_len < 1 || q_len > MLAV_MAX_Q) return MLAV_ERR_SHAPE;
+  for (int32_t i = 0; i < q_len; ++i)
+    if (!(host_parent[i] == -1 || (host_parent[i] >= 0 && host_parent[i] < i))) return MLAV_ERR_TREE;
+  return MLAV_OK;
+}
+
+int32_t mla_verify_combine(const float* part_out, const float* part_lse, int32_t nsplit,
+                           int64_t rows, float* out, float* lse, void* stream) {
+  if (!part_out || !part_lse || !out || !lse) return MLAV_ERR_NULL;
+  if (nsplit < 1 || rows < 1 || rows > (int64_t(1) << 34)) return MLAV_ERR_SHAPE;
+  if (!aligned(part_out, 16) || !aligned(out, 16) || !aligned(part_lse, 4) || !aligned(lse, 4))
+    return MLAV_ERR_ALIGN;
+  if (rows % kHeads != 0) return MLAV_ERR_SHAPE;  // rows are (token, head) pairs
+  Args a{};
+  a.part_o = const_cast<float*>(part_out);
+  a.part_lse = const_cast<float*>(part_lse);
+  a.out = out;
+  a.lse = lse;
+  a.q = (int32_t)(rows / kHeads);
+  a.batch = 1;
+  a.nsplit = nsplit;
+  a.fixed_ns = nsplit;
+  a.chunk = 1;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0,
+                     (hipStream_t)stream, a, rows);
+  return hipGetLastError() == hipSuccess ? MLAV_OK : MLAV_ERR_HIP;
+}
+
+const char* mla_verify_strerror(int32_t status) {
+  switch (status) {
+    case MLAV_OK: return "ok";
+    case MLAV_ERR_NULL: return "a required pointer is NULL";
+    case MLAV_ERR_SHAPE: return "a size is out of range";
+    case MLAV_ERR_TREE: return "tree_parent is not topologically ordered";
+    case MLAV_ERR_ALIGN: return "a pointer is not aligned (16 B for tensors, 4 B for lse/parents)";
+    case MLAV_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLAV_ERR_UNSUPPORTED: return "unsupported configuration (num_heads must be 64)";
+    case MLAV_ERR_HIP: return "HIP runtime error";
+    case MLAV_ERR_ARG: return "invalid scalar or option value";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

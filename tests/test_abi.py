@@ -1,0 +1,162 @@
+"""The C-ABI library without a GPU: it loads, exports what the header
+declares, and rejects bad arguments on the host before touching a device."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from mla_tree_verify_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_verify.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_verify\w*)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_strerror(lib):
+    assert _lib.strerror(0) == "ok"
+    for code in range(1, 9):
+        assert _lib.strerror(code) != "unknown status"
+    assert _lib.strerror(99) == "unknown status"
+
+
+def test_check_tree(lib):
+    assert _lib.check_tree([-1, 0, 0, 1, -1]) == _lib.MLAV_OK
+    assert _lib.check_tree([-1, 0, 2]) == _lib.MLAV_ERR_TREE
+    assert _lib.check_tree([0]) == _lib.MLAV_ERR_TREE
+    assert _lib.check_tree([-2]) == _lib.MLAV_ERR_TREE
+    arr = (ctypes.c_int32 * 1)(-1)
+    assert lib.mla_verify_check_tree(None, 1) == _lib.MLAV_ERR_NULL
+    assert lib.mla_verify_check_tree(arr, 0) == _lib.MLAV_ERR_SHAPE
+    assert lib.mla_verify_check_tree(arr, 65) == _lib.MLAV_ERR_SHAPE
+
+
+@pytest.mark.parametrize("q,p,cus", [(9, 256, 256), (9, 4096, 256), (9, 16384, 256), (33, 16384, 256),
+                                     (9, 65536, 256), (1, 0, 256), (64, 1, 304), (2, 31, 8), (9, 16384, 1)])
+def test_plan_properties(lib, q, p, cus):
+    n = p + q
+    pl = _lib.plan(q, 64, 1, n, n, cus)
+    assert pl.tile == 32
+    assert pl.chunk % pl.tile == 0 and pl.chunk >= pl.tile
+    assert pl.nsplit == math.ceil(n / pl.chunk)  # chunks cover [0, n) without overlap
+    assert (pl.nsplit - 1) * pl.chunk < n
+    assert pl.combine == (1 if pl.nsplit > 1 else 0)
+    nwork = q * pl.nsplit
+    assert pl.grid >= nwork and pl.grid % 8 == 0 and pl.grid - nwork < 8
+    if q >= cus:
+        assert pl.nsplit == 1
+    # about one workgroup per CU once the KV is long enough
+    if n >= 64 * cus and q <= cus:
+        assert nwork <= cus
+
+
+def test_plan_forced_split(lib):
+    pl = _lib.plan(9, 64, 1, 16393, 16393, 256, nsplit=7)
+    assert pl.nsplit <= 7 and pl.nsplit >= 6
+    pl1 = _lib.plan(9, 64, 1, 16393, 16393, 256, nsplit=1)
+    assert pl1.nsplit == 1 and pl1.combine == 0
+
+
+def test_plan_batched(lib):
+    pl = _lib.plan(33, 64, 8, 80000, 32801, 256)
+    assert pl.nsplit == math.ceil(32801 / pl.chunk)
+
+
+def test_workspace_size(lib):
+    n = 16393
+    pl = _lib.plan(9, 64, 1, n, n, 256)
+    ws = _lib.workspace_size(9, 64, 1, n, n, num_cus=256)
+    assert ws == pl.nsplit * 9 * 64 * 513 * 4
+    assert _lib.workspace_size(9, 64, 1, 265, 265, num_cus=256, nsplit=1) == 0
+    assert _lib.workspace_size(9, 32, 1, n, n, num_cus=256) == 0  # unsupported -> 0
+    assert _lib.workspace_size(0, 64, 1, n, n, num_cus=256) == 0
+
+
+def test_plan_errors(lib):
+    with pytest.raises(_lib.MLAVError) as e:
+        _lib.plan(9, 32, 1, 100, 100, 256)
+    assert e.value.status == _lib.MLAV_ERR_UNSUPPORTED
+    for args in [(0, 64, 1, 100, 100, 256), (65, 64, 1, 100, 100, 256), (9, 64, 1, 5, 5, 256),
+                 (9, 64, 2, 100, 200, 256)]:
+        with pytest.raises(_lib.MLAVError) as e:
+            _lib.plan(*args)
+        assert e.value.status == _lib.MLAV_ERR_SHAPE
+    with pytest.raises(_lib.MLAVError) as e:
+        _lib.plan(9, 64, 1, 100, 100, 0)
+    assert e.value.status == _lib.MLAV_ERR_ARG
+    with pytest.raises(_lib.MLAVError) as e:
+        _lib.plan(9, 64, 1, 100, 100, 256, pv_mode=5)
+    assert e.value.status == _lib.MLAV_ERR_ARG
+
+
+# fake, aligned addresses: validation must reject the call before any use
+A = 0x10000
+
+
+def call(lib, **kw):
+    args = dict(qn=A, qr=A, lat=A, rope=A, parent=A, prefix=100, scale=0.07, out=A, lse=A, q=9, h=64,
+                ws=None, wsb=0, stream=None)
+    args.update(kw)
+    return lib.mla_verify(args["qn"], args["qr"], args["lat"], args["rope"], args["parent"], args["prefix"],
+                          args["scale"], args["out"], args["lse"], args["q"], args["h"], args["ws"],
+                          args["wsb"], args["stream"])
+
+
+def test_host_validation_errors(lib):
+    for k in ("qn", "qr", "lat", "rope", "parent", "out", "lse"):
+        assert call(lib, **{k: None}) == _lib.MLAV_ERR_NULL
+    assert call(lib, q=0) == _lib.MLAV_ERR_SHAPE
+    assert call(lib, q=65) == _lib.MLAV_ERR_SHAPE
+    assert call(lib, h=0) == _lib.MLAV_ERR_SHAPE
+    assert call(lib, h=16) == _lib.MLAV_ERR_UNSUPPORTED
+    assert call(lib, h=128) == _lib.MLAV_ERR_UNSUPPORTED
+    assert call(lib, prefix=-1) == _lib.MLAV_ERR_SHAPE
+    for k in ("qn", "qr", "lat", "rope", "out"):
+        assert call(lib, **{k: A + 8}) == _lib.MLAV_ERR_ALIGN
+    for k in ("lse", "parent"):
+        assert call(lib, **{k: A + 2}) == _lib.MLAV_ERR_ALIGN
+    assert call(lib, scale=float("nan")) == _lib.MLAV_ERR_ARG
+    assert call(lib, scale=float("inf")) == _lib.MLAV_ERR_ARG
+    bad = _lib.Options(0, 0, 0, 1)
+    assert lib.mla_verify_ex(A, A, A, A, A, 100, 0.07, A, A, 9, 64, None, 0, None,
+                             ctypes.byref(bad)) == _lib.MLAV_ERR_ARG
+
+
+def test_batched_validation_errors(lib):
+    opt = _lib.options()
+    f = lib.mla_verify_batched
+    ok = dict(offs=A, batch=2, total=200, maxkv=100)
+
+    def c(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return f(A, A, A, A, A, d["offs"], d["batch"], d["total"], d["maxkv"], 0.07, A, A, 9, 64, None, 0,
+                 None, ctypes.byref(opt))
+
+    assert c(offs=None) == _lib.MLAV_ERR_NULL
+    assert c(offs=A + 4) == _lib.MLAV_ERR_ALIGN
+    assert c(batch=0) == _lib.MLAV_ERR_SHAPE
+    assert c(maxkv=5) == _lib.MLAV_ERR_SHAPE
+    assert c(total=10) == _lib.MLAV_ERR_SHAPE
+    assert c(maxkv=300) == _lib.MLAV_ERR_SHAPE
+
+
+def test_combine_validation(lib):
+    f = lib.mla_verify_combine
+    assert f(None, A, 2, 64, A, A, None) == _lib.MLAV_ERR_NULL
+    assert f(A, A, 0, 64, A, A, None) == _lib.MLAV_ERR_SHAPE
+    assert f(A, A, 2, 63, A, A, None) == _lib.MLAV_ERR_SHAPE
+    assert f(A + 4, A, 2, 64, A, A, None) == _lib.MLAV_ERR_ALIGN

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar, element by element: |out - ref| <= 2e-3 + 1e-2 |ref| and |lse - ref| <= 1e-3.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.mla_verify_oracle as orc
+from mla_tree_verify_amd import _lib, api, gen
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, LSE_TOL = 2e-3, 1e-2, 1e-3
+DEV = "cuda:0"
+
+
+def dev_case(case: gen.Case):
+    d = {k: getattr(case, k).to(DEV) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
+    if case.batched:
+        d["kv_offsets"] = case.kv_offsets.to(DEV)
+    return d
+
+
+def run(case: gen.Case, **kw):
+    d = dev_case(case)
+    if case.batched:
+        out, lse = api.mla_verify_batched(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"],
+                                          d["tree_parent"], d["kv_offsets"], case.scale,
+                                          max_kv=int((case.kv_offsets[1:] - case.kv_offsets[:-1]).max()), **kw)
+    else:
+        out, lse = api.mla_verify(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
+                                  case.prefix_len, case.scale, **kw)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def oracle(case: gen.Case):
+    if case.batched:
+        return orc.mla_verify_batched(case.q_nope, case.q_rope, case.kv_latent, case.k_rope, case.tree_parent,
+                                      case.kv_offsets, case.scale)
+    return orc.mla_verify(case.q_nope, case.q_rope, case.kv_latent, case.k_rope, case.tree_parent,
+                          case.prefix_len, case.scale)
+
+
+def assert_parity(out, lse, ref_out, ref_lse, label=""):
+    o = out.double().numpy()
+    l = lse.double().numpy()
+    assert np.isfinite(o).all() and np.isfinite(l).all(), f"{label}: non-finite output"
+    err = np.abs(o - ref_out)
+    tol = ATOL + RTOL * np.abs(ref_out)
+    bad = err > tol
+    assert not bad.any(), (f"{label}: {int(bad.sum())} of {bad.size} outputs off; worst err/tol "
+                           f"{(err / tol).max():.3f} at {np.unravel_index((err / tol).argmax(), err.shape)}")
+    lerr = np.abs(l - ref_lse).max()
+    assert lerr <= LSE_TOL, f"{label}: lse max err {lerr:.2e}"
+
+
+# ---------------------------------------------------------------------------
+# small and edge shapes: prefix around tile (32) and chunk boundaries, q from 1 to 64
+# ---------------------------------------------------------------------------
+EDGE = [
+    (1, 0, "random"), (1, 1, "star"), (2, 0, "chain"), (5, 0, "star"), (9, 0, "random"),
+    (9, 1, "random"), (9, 22, "random"), (9, 23, "chain"), (9, 24, "random"), (9, 31, "random"),
+    (9, 32, "star"), (9, 33, "random"), (9, 55, "random"), (9, 63, "chain"), (9, 64, "random"),
+    (9, 65, "random"), (9, 100, "bounded"), (9, 256, "random"), (9, 1000, "random"),
+    (33, 0, "bounded"), (33, 31, "bounded"), (33, 128, "random"), (33, 512, "bounded"),
+    (33, 2048, "bounded"), (64, 0, "random"), (64, 7, "chain"), (64, 300, "random"), (64, 1000, "star"),
+    (17, 4096, "random"), (3, 9999, "chain"),
+]
+
+
+@pytest.mark.parametrize("q,p,tree", EDGE)
+def test_edge_shapes(q, p, tree):
+    case = gen.make_case(q, p, tree=tree, seed=1000 + 7 * q + p)
+    out, lse = run(case)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, f"q{q} p{p} {tree}")
+
+
+@pytest.mark.parametrize("name", sorted(gen.WORKLOADS))
+def test_workloads_full_size(name):
+    case = gen.make_workload(name)
+    out, lse = run(case)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, name)
+
+
+def test_chunk_boundaries():
+    pl = api.device_plan(9, 1, 16393, 16393)
+    c = int(pl.chunk)
+    for n in (c - 1, c, c + 1, 2 * c - 1, 2 * c + 1):
+        case = gen.make_case(9, n - 9, tree="random", seed=n)
+        out, lse = run(case)
+        ro, rl = oracle(case)
+        assert_parity(out, lse, ro, rl, f"n={n} (chunk {c})")
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+def test_split_count_invariance():
+    case = gen.make_case(9, 3000, tree="random", seed=77)
+    ro, rl = oracle(case)
+    outs = {}
+    for ns in (1, 2, 3, 7, 0, 94):
+        out, lse = run(case, nsplit=ns)
+        assert_parity(out, lse, ro, rl, f"nsplit={ns}")
+        outs[ns] = (out, lse)
+    base_o, base_l = outs[1]
+    scale = base_o.abs().max().item()
+    for ns, (o, l) in outs.items():
+        assert (o - base_o).abs().max().item() <= 1e-5 * scale + 1e-6, f"nsplit {ns} differs"
+        assert (l - base_l).abs().max().item() <= 1e-5
+
+
+def test_masked_tree_rows_do_not_matter_bitwise():
+    case = gen.make_case(9, 700, tree="random", seed=5)
+    out, lse = run(case)
+    anc = orc.ancestors_inclusive(case.tree_parent.tolist())
+    for i in range(9):
+        c2 = gen.make_case(9, 700, tree="random", seed=5)
+        for u in range(9):
+            if u not in anc[i]:
+                c2.kv_latent[700 + u] = 1e4 if u % 2 else -1e4
+                c2.k_rope[700 + u] = -1e4 if u % 2 else 1e4
+        o2, l2 = run(c2)
+        assert torch.equal(o2[i], out[i]) and torch.equal(l2[i], lse[i]), f"token {i} changed"
+
+
+def test_head_permutation():
+    case = gen.make_case(9, 500, tree="random", seed=9)
+    out, lse = run(case)
+    perm = torch.randperm(64, generator=torch.Generator().manual_seed(3))
+    c2 = gen.make_case(9, 500, tree="random", seed=9)
+    c2.q_nope = c2.q_nope[:, perm].contiguous()
+    c2.q_rope = c2.q_rope[:, perm].contiguous()
+    o2, l2 = run(c2)
+    assert (o2 - out[:, perm]).abs().max().item() <= 1e-6
+    assert (l2 - lse[:, perm]).abs().max().item() <= 1e-6
+
+
+def test_run_to_run_bitwise():
+    case = gen.make_workload("q9_p4096")
+    o1, l1 = run(case)
+    o2, l2 = run(case)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_batched_equals_per_sequence():
+    case = gen.make_batched_case(4, 9, prefix_lens=[100, 3000, 33, 1500], tree="random", seed=21)
+    out, lse = run(case)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, "batched")
+    offs = case.kv_offsets.tolist()
+    for b in range(4):
+        single = gen.Case(q_nope=case.q_nope[b].contiguous(), q_rope=case.q_rope[b].contiguous(),
+                          kv_latent=case.kv_latent[offs[b]:offs[b + 1]].contiguous(),
+                          k_rope=case.k_rope[offs[b]:offs[b + 1]].contiguous(),
+                          tree_parent=case.tree_parent[b].contiguous(), prefix_len=offs[b + 1] - offs[b] - 9,
+                          scale=case.scale)
+        o, l = run(single)
+        assert_parity(o, l, ro[b], rl[b], f"seq {b}")
+
+
+def test_bad_offsets_give_nan_not_fault():
+    case = gen.make_batched_case(2, 9, prefix_lens=[100, 200], tree="random", seed=2)
+    d = dev_case(case)
+    bad = case.kv_offsets.clone()
+    bad[1] = 5  # sequence 0 shorter than its tree
+    out, lse = api.mla_verify_batched(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
+                                      bad.to(DEV), case.scale, max_kv=300)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0]).all() and torch.isnan(lse[0]).all()
+
+
+# ---------------------------------------------------------------------------
+# numerically special inputs
+# ---------------------------------------------------------------------------
+def test_reference_max_restart():
+    """A late key whose score is far above the first tile's max (beyond 2^64
+    in weight) takes the redo-the-chunk path; the result stays exact."""
+    case = gen.make_case(3, 200, tree="chain", seed=31, num_heads=64)
+    case.kv_latent[150] = (case.q_nope[0, 0].float() * 0.5).to(torch.bfloat16)
+    case.k_rope[150] = (case.q_rope[0, 0].float() * 0.5).to(torch.bfloat16)
+    case.scale = 1.0
+    out, lse = run(case)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, "restart")
+
+
+def test_peaky_single_key_dominates():
+    case = gen.make_case(9, 777, tree="random", seed=41)
+    case.scale = 4.0  # nearly one-hot softmax rows
+    out, lse = run(case)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, "one-hot")
+
+
+def test_single_bf16_weight_mode_on_normal_inputs():
+    case = gen.make_workload("q9_p4096")
+    out, lse = run(case, pv_mode=1)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, "pv_mode=1")
+
+
+# ---------------------------------------------------------------------------
+# the second (VALU) kernel and the combine kernel on their own
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("q,p,tree", [(9, 0, "star"), (9, 33, "random"), (33, 700, "bounded"), (9, 5000, "chain")])
+def test_valu_kernel(q, p, tree):
+    case = gen.make_case(q, p, tree=tree, seed=p + q)
+    out, lse = run(case, kernel=1)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, f"valu q{q} p{p}")
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 5, 28, 64])
+def test_combine_kernel_on_synthetic_partials(nsplit):
+    g = torch.Generator().manual_seed(nsplit)
+    rows = 128
+    part = torch.randn(nsplit, rows, 512, generator=g, dtype=torch.float32) * 3
+    plse = torch.randn(nsplit, rows, generator=g, dtype=torch.float32) * 20
+    if nsplit > 1:
+        plse[0, :7] = -math.inf  # empty parts
+        plse[:, 5] = -math.inf  # a row with nothing at all
+    out, lse = api.combine(part.to(DEV), plse.to(DEV))
+    torch.cuda.synchronize()
+    ro, rl = orc.lse_merge(list(part.double().numpy()), list(plse.double().numpy()))
+    o = out.cpu().double().numpy()
+    assert np.abs(o - ro).max() <= 1e-5 * max(1.0, np.abs(ro).max())
+    l = lse.cpu().double().numpy()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(l), fin)
+    assert np.abs(l[fin] - rl[fin]).max() <= 1e-5 * max(1.0, np.abs(rl[fin]).max())
+
+
+def test_workspace_too_small_is_rejected():
+    case = gen.make_workload("q9_p16384")
+    d = dev_case(case)
+    with pytest.raises(_lib.MLAVError) as e:
+        api.mla_verify(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
+                       case.prefix_len, case.scale, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == _lib.MLAV_ERR_WORKSPACE
