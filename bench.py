@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of absorbed-MLA tree-verify attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q9_p16384]
+
+One step = one full verify call (split-KV MFMA kernel + combine kernel) over one
+batch of synthetic bf16 inputs already resident in HBM. Prints one JSON line:
+value = algorithmic TFLOP/s of the whole call, measured on rotating input
+copies (more bytes than the 256 MB MALL, so every call reads its KV from HBM);
+the warm figure (same inputs every call) is reported beside it. `roofline`
+covers the split kernel, timed alone with HIP events on its stream;
+`cpu_baseline` times the fp64 oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+SRC = os.path.join(ROOT, "mla_tree_verify_amd", "csrc", "mla_verify.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+# the pages' final sm_120 kernel at q_len 9, prefix 16384 (fp32, RTX PRO 6000): 4782.6 us
+PAGES_US_Q9_P16384 = 4782.6
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="q9_p16384")
+    ap.add_argument("--rotate-mb", type=float, default=768.0, help="bytes of rotating input copies (cold run)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target host time of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=float, default=0.0,
+                    help="after timing, run one device copy of this size (counter calibration)")
+    ap.add_argument("--pv-mode", type=int, default=0)
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per split-kernel launch from the committed counter summary,
+    or None when there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"split_mfma_kernel_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_digest():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the verify operator has no "
+                          "multi-GPU path here (see the sharding notes in DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import oracle.mla_verify_oracle as orc
+    from mla_tree_verify_amd import _lib, api, gen
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = gen.WORKLOADS[args.workload]
+    if spec["kind"] != "single":
+        print(json.dumps({"error": "bench.py times single-sequence workloads"}))
+        return 2
+    case = gen.make_workload(args.workload)
+    q, p = case.q_len, case.prefix_len
+    n = p + q
+    flops = orc.algorithmic_flops(case.tree_parent, p)
+    alg_bytes = orc.algorithmic_bytes(q, n)
+    plan = api.device_plan(q, 1, n, n, pv_mode=args.pv_mode)
+
+    host = {k: getattr(case, k) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
+    per_copy = sum(t.numel() * t.element_size() for t in host.values()) + q * 64 * 513 * 4 * (plan.nsplit + 1)
+    ncopy = max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))
+    copies = []
+    for _ in range(ncopy):
+        d = {k: v.to(dev) for k, v in host.items()}
+        d["out"] = torch.empty(q, 64, 512, dtype=torch.float32, device=dev)
+        d["lse"] = torch.empty(q, 64, dtype=torch.float32, device=dev)
+        ws = _lib.workspace_size(q, 64, 1, n, n, pv_mode=args.pv_mode)
+        d["ws"] = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+        d["po"] = torch.empty(plan.nsplit, q, 64, 512, dtype=torch.float32, device=dev)
+        d["pl"] = torch.empty(plan.nsplit, q, 64, dtype=torch.float32, device=dev)
+        copies.append(d)
+    stream = torch.cuda.current_stream(dev)
+
+    def call(d):
+        api.mla_verify(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], p, case.scale,
+                       out=d["out"], lse=d["lse"], workspace=d["ws"], pv_mode=args.pv_mode)
+
+    def timed(rotate: bool) -> float:
+        for i in range(args.warmup):
+            call(copies[i % ncopy] if rotate else copies[0])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            call(copies[i % ncopy] if rotate else copies[0])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps  # us per call
+
+    us_warm = timed(rotate=False)
+    us_cold = timed(rotate=True)
+
+    # split kernel alone: events around each launch on the stream it runs on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup):
+        d = copies[i % ncopy]
+        api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], p,
+                                case.scale, plan, part_out=d["po"], part_lse=d["pl"], pv_mode=args.pv_mode)
+        if plan.nsplit > 1:
+            api.combine(d["po"], d["pl"], out=d["out"].view(-1, 512), lse=d["lse"].view(-1))
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        d = copies[i % ncopy]
+        ev[i][0].record(stream)
+        api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], p,
+                                case.scale, plan, part_out=d["po"], part_lse=d["pl"], pv_mode=args.pv_mode)
+        ev[i][1].record(stream)
+        if plan.nsplit > 1:
+            api.combine(d["po"], d["pl"], out=d["out"].view(-1, 512), lse=d["lse"].view(-1))
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    split_us = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
+    combine_us = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+
+    if args.copy_calib_mb > 0:
+        nb = int(args.copy_calib_mb * 2**20) // 4 * 4
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # parity of the benchmarked output against the oracle (also the CPU baseline)
+    d0 = copies[0]
+    call(d0)
+    torch.cuda.synchronize()
+    out = d0["out"].cpu().double().numpy()
+    lse = d0["lse"].cpu().double().numpy()
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        reps, t_cpu = 0, 0.0
+        ro = rl = None
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            ro, rl = orc.mla_verify(case.q_nope, case.q_rope, case.kv_latent, case.k_rope, case.tree_parent, p,
+                                    case.scale)
+            t_cpu += time.perf_counter() - t0
+            reps += 1
+            if t_cpu >= args.cpu_seconds or time.perf_counter() - t_start > 30.0:
+                break
+        cpu = {"value": flops * reps / t_cpu / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"the full {args.workload} workload, {reps} oracle call(s), fp64 numpy, "
+                         f"{t_cpu:.1f} s; us/call {t_cpu / reps * 1e6:.0f}"}
+        err = np.abs(out - ro)
+        parity = {"max_abs_err": float(err.max()),
+                  "worst_err_over_tol": float((err / (2e-3 + 1e-2 * np.abs(ro))).max()),
+                  "lse_max_abs_err": float(np.abs(lse - rl).max())}
+
+    tflops = flops / (us_cold * 1e-6) / 1e12
+    tflops_warm = flops / (us_warm * 1e-6) / 1e12
+    achieved = flops / (split_us * 1e-6) / 1e12
+    traffic = read_traffic(args.workload)
+    res = {
+        "metric": "MLA verify attention us/call + TFLOP/s (% MFMA peak), H=64 q_len=9, prefix 16k",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_cold / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / (flops / (PAGES_US_Q9_P16384 * 1e-6) / 1e12), 2)
+        if args.workload == "q9_p16384" else None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": n, "heads": 64, "dl": 512,
+                   "dr": 64, "tree": case.meta["tree"], "scale": case.scale, "nsplit": plan.nsplit,
+                   "chunk": plan.chunk, "pv_mode": args.pv_mode, "parallelism": "single GPU"},
+        "us_per_call": round(us_cold, 2),
+        "us_per_call_warm": round(us_warm, 2),
+        "tflops_warm": round(tflops_warm, 2),
+        "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "hbm_gbs_algorithmic": round(alg_bytes / (us_cold * 1e-6) / 1e9, 1),
+        "pct_hbm_peak": round(100 * alg_bytes / (us_cold * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+        "split_kernel_us": round(split_us, 2),
+        "combine_kernel_us": round(combine_us, 2),
+        "algorithmic_gflop": round(flops / 1e9, 3),
+        "algorithmic_mb": round(alg_bytes / 1e6, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "split_mfma_kernel", "algorithmic_flop_per_launch": flops},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "baseline_note": "vs_baseline divides by the pages' final sm_120 kernel at q9/16k (4782.6 us, fp32, RTX PRO "
+                         "6000): context from other hardware, not a target",
+    }
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

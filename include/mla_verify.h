@@ -68,6 +68,8 @@ extern "C" {
 #define MLAV_HEADS 64    /* the head count the kernels are built for */
 #define MLAV_DL 512      /* latent width (value width) */
 #define MLAV_DR 64       /* rope width */
+#define MLAV_MAX_KV 4000000 /* KV rows per sequence (byte offsets into one sequence's
+                               latent rows must stay below 2^32) */
 
 /* Tuning knobs; a NULL options pointer means all zeros. */
 typedef struct mlav_options {
@@ -86,7 +88,7 @@ typedef struct mlav_options {
 typedef struct mlav_plan {
   int32_t nsplit;  /* KV splits per sequence (of the longest sequence) */
   int32_t tile;    /* keys per wave tile */
-  int64_t chunk;   /* keys per split (a multiple of 2*tile) */
+  int64_t chunk;   /* keys per split (a multiple of tile) */
   int32_t grid;    /* workgroups of the split kernel */
   int32_t combine; /* 1 when the combine kernel runs (nsplit > 1) */
 } mlav_plan;
@@ -98,7 +100,7 @@ typedef struct mlav_plan {
  *   kv_latent       [prefix_len + q_len, 512] bf16 latent keys = values
  *   k_rope          [prefix_len + q_len, 64]  bf16 rope keys
  *   tree_parent     [q_len] int32
- *   prefix_len      >= 0 cached tokens before the tree
+ *   prefix_len      >= 0 cached tokens before the tree; prefix_len + q_len <= MLAV_MAX_KV
  *   scale           fp32 factor on the whole 576-d dot product
  *   out             [q_len, num_heads, 512] fp32
  *   lse             [q_len, num_heads] fp32, natural log
@@ -146,6 +148,27 @@ size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch
 int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
                         int64_t max_kv, int32_t num_cus, const mlav_options* opt,
                         mlav_plan* plan_out);
+
+/*
+ * The split phase alone, for a caller-chosen plan (from mla_verify_plan):
+ * each KV chunk of plan->chunk keys yields a normalised partial output and its
+ * lse (the "unnormalised accumulator and statistics" of each split, page "The
+ * Decisive Microbench", section "The KV-Split Solution", here stored
+ * normalised) in
+ *   part_out [plan->nsplit, q_len, num_heads, 512] fp32 and
+ *   part_lse [plan->nsplit, q_len, num_heads] fp32 (natural log).
+ * mla_verify_combine(part_out, part_lse, plan->nsplit, q_len * num_heads, ...)
+ * then gives exactly what mla_verify returns. Partials from several callers
+ * (e.g. KV shards) can be stacked and combined the same way; a split that sees
+ * no visible key has lse = -inf and a zero output. The plan must satisfy
+ * nsplit = ceil((prefix_len + q_len) / chunk) with chunk a positive multiple of
+ * plan->tile (32); otherwise MLAV_ERR_ARG. Other arguments as for mla_verify.
+ */
+int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                            const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
+                            float scale, float* part_out, float* part_lse, int32_t q_len,
+                            int32_t num_heads, const mlav_plan* plan, void* stream,
+                            const mlav_options* opt);
 
 /* Host-side check of a HOST copy of a tree: MLAV_OK or MLAV_ERR_TREE. */
 int32_t mla_verify_check_tree(const int32_t* host_parent, int32_t q_len);

@@ -6,7 +6,7 @@
 The library (libmla_verify.so, built by `python -m mla_tree_verify_amd.build`)
 is loaded on first use; there is no CPU fallback.
 """
-_API = ("mla_verify", "mla_verify_batched", "combine", "device_plan")
+_API = ("mla_verify", "mla_verify_batched", "mla_verify_partials", "combine", "device_plan")
 
 
 def __getattr__(name):

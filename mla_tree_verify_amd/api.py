@@ -121,11 +121,44 @@ def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: to
     return out, lse
 
 
+def mla_verify_partials(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tensor,
+                        k_rope: torch.Tensor, tree_parent: torch.Tensor, prefix_len: int, scale: float,
+                        plan: _lib.Plan, part_out: Optional[torch.Tensor] = None,
+                        part_lse: Optional[torch.Tensor] = None, pv_mode: int = 0, kernel: int = 0):
+    """The split phase for `plan`: part_out [S, q, H, 512], part_lse [S, q, H] (fp32)."""
+    dev = q_nope.device
+    q, h = int(q_nope.shape[0]), int(q_nope.shape[1])
+    n = int(prefix_len) + q
+    _check(q_nope, "q_nope", torch.bfloat16, (q, h, DL), dev)
+    _check(q_rope, "q_rope", torch.bfloat16, (q, h, DR), dev)
+    _check(kv_latent, "kv_latent", torch.bfloat16, (n, DL), dev)
+    _check(k_rope, "k_rope", torch.bfloat16, (n, DR), dev)
+    _check(tree_parent, "tree_parent", torch.int32, (q,), dev)
+    s = int(plan.nsplit)
+    if part_out is None:
+        part_out = torch.empty(s, q, h, DL, dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty(s, q, h, dtype=torch.float32, device=dev)
+    _check(part_out, "part_out", torch.float32, (s, q, h, DL), dev)
+    _check(part_lse, "part_lse", torch.float32, (s, q, h), dev)
+    opt = _lib.options(0, pv_mode, kernel)
+    rc = _lib.load().mla_verify_partials(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(),
+                                         k_rope.data_ptr(), tree_parent.data_ptr(), int(prefix_len),
+                                         float(scale), part_out.data_ptr(), part_lse.data_ptr(), q, h,
+                                         ctypes.byref(plan), _stream_ptr(dev), ctypes.byref(opt))
+    if rc != _lib.MLAV_OK:
+        raise _lib.MLAVError(rc, "mla_verify_partials")
+    return part_out, part_lse
+
+
 def combine(part_out: torch.Tensor, part_lse: torch.Tensor,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """LSE merge of caller-made partials: part_out [S, rows, 512], part_lse [S, rows]."""
     dev = part_out.device
-    s, rows = int(part_out.shape[0]), int(part_out.shape[1])
+    s = int(part_out.shape[0])
+    part_out = part_out.reshape(s, -1, DL)
+    part_lse = part_lse.reshape(s, -1)
+    rows = int(part_out.shape[1])
     _check(part_out, "part_out", torch.float32, (s, rows, DL), dev)
     _check(part_lse, "part_lse", torch.float32, (s, rows), dev)
     if out is None:

@@ -572,7 +572,7 @@ int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t
   if (q < 1 || q > MLAV_MAX_Q || batch < 1 || heads < 1) return MLAV_ERR_SHAPE;
   if (heads != kHeads) return MLAV_ERR_UNSUPPORTED;
   if (max_kv < q || total_kv < (int64_t)batch * q || max_kv > total_kv) return MLAV_ERR_SHAPE;
-  if (max_kv > (int64_t(1) << 40)) return MLAV_ERR_SHAPE;
+  if (max_kv > MLAV_MAX_KV) return MLAV_ERR_SHAPE;
   if (num_cus < 1) return MLAV_ERR_ARG;
   const int rc = check_options(opt);
   if (rc != MLAV_OK) return rc;
@@ -683,7 +683,7 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
   int rc = common_checks(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, scale, out, lse,
                          q_len, num_heads, opt);
   if (rc != MLAV_OK) return rc;
-  if (prefix_len < 0 || prefix_len > (int64_t(1) << 40)) return MLAV_ERR_SHAPE;
+  if (prefix_len < 0 || prefix_len + q_len > MLAV_MAX_KV) return MLAV_ERR_SHAPE;
   const int64_t n = prefix_len + q_len;
   int32_t cus = 0;
   rc = device_cus(&cus);
@@ -762,6 +762,46 @@ int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, cons
   a.scale_log2 = scale * kLog2e;
   a.q = q_len;
   a.batch = batch;
+  return launch(a, p, opt, stream);
+}
+
+int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                            const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
+                            float scale, float* part_out, float* part_lse, int32_t q_len,
+                            int32_t num_heads, const mlav_plan* plan, void* stream,
+                            const mlav_options* opt) {
+  int rc = common_checks(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, scale, part_out,
+                         part_lse, q_len, num_heads, opt);
+  if (rc != MLAV_OK) return rc;
+  if (!plan) return MLAV_ERR_NULL;
+  if (prefix_len < 0 || prefix_len + q_len > MLAV_MAX_KV) return MLAV_ERR_SHAPE;
+  const int64_t n = prefix_len + q_len;
+  if (plan->tile != kTile || plan->chunk < kTile || plan->chunk % kTile != 0 || plan->nsplit < 1 ||
+      plan->nsplit != (n + plan->chunk - 1) / plan->chunk)
+    return MLAV_ERR_ARG;
+  mlav_plan p = *plan;
+  const int kernel = opt ? opt->kernel : 0;
+  const int64_t nwork = (int64_t)q_len * p.nsplit;
+  p.grid = kernel == 0 ? (int32_t)((nwork + kXcds - 1) / kXcds * kXcds) : (int32_t)(nwork * 16);
+  p.combine = 0;
+  Args a{};
+  a.qn = (const uint16_t*)q_nope_absorbed;
+  a.qr = (const uint16_t*)q_rope;
+  a.lat = (const uint16_t*)kv_latent;
+  a.rope = (const uint16_t*)k_rope;
+  a.parent = tree_parent;
+  a.offs = nullptr;
+  // with one split the partial is the final result; the layouts coincide
+  a.out = part_out;
+  a.lse = part_lse;
+  a.part_o = part_out;
+  a.part_lse = part_lse;
+  a.single_n = n;
+  a.total_kv = n;
+  a.max_kv = n;
+  a.scale_log2 = scale * kLog2e;
+  a.q = q_len;
+  a.batch = 1;
   return launch(a, p, opt, stream);
 }
 

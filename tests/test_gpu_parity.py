@@ -246,3 +246,33 @@ def test_workspace_too_small_is_rejected():
         api.mla_verify(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
                        case.prefix_len, case.scale, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert e.value.status == _lib.MLAV_ERR_WORKSPACE
+
+
+def test_partials_then_combine_equals_full_call():
+    case = gen.make_workload("q9_p16384")
+    d = dev_case(case)
+    out, lse = run(case)
+    pl = api.device_plan(case.q_len, 1, case.prefix_len + case.q_len, case.prefix_len + case.q_len)
+    po, pls = api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
+                                      case.prefix_len, case.scale, pl)
+    o2, l2 = api.combine(po, pls)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu().view_as(out), out) and torch.equal(l2.cpu().view_as(lse), lse)
+
+
+def test_partials_merge_like_the_oracle_merge():
+    """Forced 4-way split: the combine kernel and the oracle's merge formula
+    give the same result from the same partials, and both match the oracle."""
+    case = gen.make_case(9, 4000, tree="random", seed=88)
+    ro, rl = oracle(case)
+    d = dev_case(case)
+    q = case.q_len
+    pl = api.device_plan(q, 1, 4000 + q, 4000 + q, nsplit=4)
+    po, pls = api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
+                                      4000, case.scale, pl)
+    o_all, l_all = api.combine(po, pls)
+    torch.cuda.synchronize()
+    assert_parity(o_all.cpu().view(q, 64, 512), l_all.cpu().view(q, 64), ro, rl, "4 partials")
+    m_o, m_l = orc.lse_merge(list(po.cpu().double().numpy()), list(pls.cpu().double().numpy()))
+    assert np.abs(m_o - o_all.cpu().view(q, 64, 512).double().numpy()).max() <= 1e-5
+    assert np.abs(m_l - l_all.cpu().view(q, 64).double().numpy()).max() <= 1e-5
