@@ -101,7 +101,7 @@ typedef struct mlav_plan {
  *   k_rope          [prefix_len + q_len, 64]  bf16 rope keys
  *   tree_parent     [q_len] int32
  *   prefix_len      >= 0 cached tokens before the tree; prefix_len + q_len <= MLAV_MAX_KV
- *   scale           fp32 factor on the whole 576-d dot product
+ *   scale           fp32 factor (> 0) on the whole 576-d dot product
  *   out             [q_len, num_heads, 512] fp32
  *   lse             [q_len, num_heads] fp32, natural log
  *   q_len           1 .. 64;  num_heads must be 64

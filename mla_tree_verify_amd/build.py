@@ -36,6 +36,8 @@ def compile_flags(resource_usage: bool = False):
         "-shared",
         "-I", INCLUDE,
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # latency-oriented machine scheduling: keeps several LDS reads in flight ahead of the MFMAs
+        "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
         "-Wno-unused-result",
     ]
     if resource_usage:

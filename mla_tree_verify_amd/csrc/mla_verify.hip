@@ -47,6 +47,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "mla_verify.h"
 
@@ -131,10 +132,35 @@ __device__ inline bool key_visible(int64_t j, int64_t c1, int64_t prefix, uint64
   return j < c1 && (j < prefix || ((anc >> (j - prefix)) & 1ull));
 }
 
+// Visibility of the 32 keys [key0, key0 + 32) for one draft token, as a bit
+// mask (bit k: key key0 + k). Keys below `prefix` are the cached prefix; key
+// prefix + u is tree node u, visible when bit u of `anc` is set; keys at or
+// past c1 (the chunk end) are not part of this chunk. All operands are
+// wave-uniform, so this is scalar work.
+__device__ inline uint32_t tile_visibility(int64_t key0, int64_t c1, int64_t prefix, uint64_t anc) {
+  const int64_t np = prefix - key0;  // tile keys inside the prefix
+  uint32_t m;
+  if (np >= 32) {
+    m = 0xffffffffu;
+  } else {
+    m = np > 0 ? ((1u << np) - 1u) : 0u;
+    const int64_t sh = key0 - prefix;  // tree node at bit 0 (negative: inside the prefix)
+    uint64_t tm;
+    if (sh >= 0)
+      tm = sh < 64 ? (anc >> sh) : 0ull;
+    else
+      tm = -sh < 64 ? (anc << -sh) : 0ull;
+    m |= (uint32_t)tm;
+  }
+  const int64_t nv = c1 - key0;  // tile keys before the chunk end
+  if (nv < 32) m &= nv > 0 ? ((1u << nv) - 1u) : 0u;
+  return m;
+}
+
 // Logical <-> physical 16-byte chunk swizzle inside a key row (low 3 bits only).
 __device__ inline int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
 
-__device__ inline float fmax3(float a, float b) { return a > b ? a : b; }
+__device__ inline float fmax3(float a, float b) { return __builtin_fmaxf(a, b); }
 
 __device__ inline float partner_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -202,49 +228,61 @@ __device__ inline void issue_tile(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_r
                                            (key_rel + 8 * wave) * 128 + rope_voff, 0, 0, 0);
 }
 
-// Partial scores of one tile over this wave's half of the 576 dims:
-// S^T[32 keys x 32 heads] = K[32 keys x 288] Q^T[288 x 32 heads].
-// Lane layout (A operand): key lane&31, dims 16 ks + 8 (lane>>5) of the half.
-template <int kDh>
-__device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&qreg)[18], int key,
-                                       int half) {
-  f32x16_t sc = {};
-  const int sw = swz(key);
+// Lane bases of the K operand reads. Score k-step ks of a wave reads 16-byte
+// chunk c = 36 kDh + 2 ks + (lane>>5) of key lane&31's 576-d row (chunks
+// 0..63 latent, 64..71 rope), stored at chunk position c ^ swz(key) (low 3
+// bits). Since 36 kDh + 2 ks is even, that position is
+// (c & ~7) | (e2 ^ hs) with e2 = (36 kDh + 2 ks) & 7 and hs = (lane>>5) ^ swz(key),
+// so four per-lane bases (one per e2) plus a compile-time offset cover all
+// k-steps.
+struct KBases {
+  int lat[4];   // key * 1024 + 16 * ((2e) ^ hs)
+  int rope[4];  // kLatBytes + key * 128 + 16 * ((2e) ^ hs)
+};
+
+__device__ inline KBases make_kbases(int key, int half) {
+  KBases kb;
+  const int hs = half ^ swz(key);
 #pragma unroll
-  for (int ks = 0; ks < 18; ++ks) {
-    const int c = 36 * kDh + 2 * ks + half;  // logical 16-byte chunk of the 576-d row
-    int off;
-    if (36 * kDh + 2 * ks < 64)
-      off = key * 1024 + 16 * ((c & ~7) | ((c & 7) ^ sw));
-    else
-      off = kLatBytes + key * 128 + 16 * ((c - 64) ^ sw);
-    const bf16x8_t kv = *(const LDS_AS bf16x8_t*)(buf + off);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[ks], sc, 0, 0, 0);
+  for (int e = 0; e < 4; ++e) {
+    kb.lat[e] = key * 1024 + 16 * ((2 * e) ^ hs);
+    kb.rope[e] = kLatBytes + key * 128 + 16 * ((2 * e) ^ hs);
   }
-  return sc;
+  return kb;
 }
 
-// Values of one tile for this wave's 256 output dims:
-// O^T[256 dims x 32 heads] += V^T[256 x 32 keys] P^T[32 keys x 32 heads].
-// V^T comes from the latent rows through transposing LDS reads.
-template <int kDh, bool kHiLo>
-__device__ inline void tile_values(f32x16_t (&acc)[8], const LDS_AS char* buf, int pv_off_even,
-                                   int pv_off_odd, const bf16x8_t (&p_hi)[2],
-                                   const bf16x8_t (&p_lo)[2]) {
+// Byte offset (within a ring slot) of this lane's K operand for k-step ks.
+template <int kDh>
+__device__ inline int k_frag_off(const KBases& kb, int ks) {
+  const int c0 = 36 * kDh + 2 * ks;  // even chunk index of the pair
+  if (c0 < 64) return kb.lat[(c0 & 7) >> 1] + 16 * (c0 & ~7);
+  return kb.rope[((c0 - 64) & 7) >> 1];
+}
+
+__device__ inline bf16x8_t lds_b128(const LDS_AS char* p) { return *(const LDS_AS bf16x8_t*)p; }
+
+// V^T operand of value fragment j (dim block j&7 of this wave's 256 dims, key
+// step j>>3), read from the latent rows with two transposing LDS reads.
+template <int kDh>
+__device__ inline bf16x8_t v_frag(const LDS_AS char* buf, int pv_off_even, int pv_off_odd, int j) {
+  const int dbg = 8 * kDh + (j & 7);
+  const int base = ((dbg & 1) ? pv_off_odd : pv_off_even) + 128 * (dbg >> 1) + 16 * 1024 * (j >> 3);
+  const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(buf + base));
+  const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(buf + base + 8 * 1024));
+  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Partial scores of one tile over this wave's half of the 576 dims:
+// S^T[32 keys x 32 heads] = K[32 keys x 288] Q^T[288 x 32 heads].
+template <int kDh>
+__device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&qreg)[18],
+                                       const KBases& kb) {
+  f32x16_t sc = {};
 #pragma unroll
-  for (int ks2 = 0; ks2 < 2; ++ks2) {
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      constexpr int kDb0 = 8 * kDh;
-      const int dbg = kDb0 + db;
-      const int base = ((dbg & 1) ? pv_off_odd : pv_off_even) + 128 * (dbg >> 1) + 16 * 1024 * ks2;
-      const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(buf + base));
-      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(buf + base + 8 * 1024));
-      const bf16x8_t vt = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, p_hi[ks2], acc[db], 0, 0, 0);
-      if (kHiLo) acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, p_lo[ks2], acc[db], 0, 0, 0);
-    }
-  }
+  for (int ks = 0; ks < 18; ++ks)
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(buf + k_frag_off<kDh>(kb, ks)), qreg[ks], sc,
+                                                 0, 0, 0);
+  return sc;
 }
 
 // One workgroup = one draft token x 64 heads x one KV chunk; 4 waves =
@@ -294,7 +332,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
 
   LDS_AS float* xs = (LDS_AS float*)(lds + kRing * kTileBytes);  // [2][4 waves][16][64]
   const int partner = wave ^ 1;  // same head half, other dim half
-  const int key = lane & 31;
+  const KBases kb = make_kbases(lane & 31, half);
 
   // Online softmax with a reference max that never moves inside the loop: the
   // first visible tile fixes it, later weights are 2^(s - m_ref), exact for
@@ -305,6 +343,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
   float m_ref = -INFINITY;  // log2 units, this lane's head
   float l_run = 0.f;        // this lane's share of the softmax denominator
   float m_seen = -INFINITY;
+  const float sl2 = a.scale_log2;  // > 0, so max(s) * sl2 = max(s * sl2)
   for (int attempt = 0; attempt < 2; ++attempt) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[db] = (f32x16_t){};
@@ -317,62 +356,142 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
     if (ntiles > 1) issue_tile(lds + kTileBytes, lat_rs, rope_rs, kTile, wave, lane, rope_voff);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    f32x16_t own = tile_scores<kDh>(lds, qreg, key, half);
+    f32x16_t own = tile_scores<kDh>(lds, qreg, kb);
     {
       LDS_AS float* dst = xs + (0 * 4 + wave) * 1024;
 #pragma unroll
       for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = own[r];
     }
 
-    for (int i = 0; i < ntiles; ++i) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // tile i+1 landed (this wave's part)
-      __syncthreads();  // all parts landed; partial scores of tile i published; slot (i+2)%3 free
+    // One step: softmax and values of tile i, scores of tile i+1 (computed
+    // even past the last tile, on whatever that ring slot holds, and unused
+    // then). The body is an explicit software pipeline over MFMA slots: each
+    // LDS operand is read four MFMAs before its use, and the softmax
+    // arithmetic is cut into slices of about one MFMA's duration that issue
+    // behind the MFMAs. sched_barrier fences keep the slots in this order.
+    // kMasked selects the per-key visibility test.
+    auto step = [&](auto masked_tag, int i, uint32_t vis) {
+      constexpr bool kMasked = decltype(masked_tag)::value;
+      constexpr int kAhead = 4;
+      const LDS_AS char* kbuf = lds + ((i + 1) % kRing) * kTileBytes;
+      const LDS_AS char* vbuf = lds + (i % kRing) * kTileBytes;
+      const LDS_AS float* src = xs + ((i & 1) * 4 + partner) * 1024;
+      LDS_AS float* dst = xs + (((i + 1) & 1) * 4 + wave) * 1024;
+
+      float part[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[r] = src[r * 64 + lane];
+      bf16x8_t kf[18];
+#pragma unroll
+      for (int ks = 0; ks < kAhead; ++ks) kf[ks] = lds_b128(kbuf + k_frag_off<kDh>(kb, ks));
+      __builtin_amdgcn_sched_barrier(0);
+
+      f32x16_t sc = {};
+      float sv[16], pw[16];
+      float smax = 0.f, mref = 0.f;
+      bf16x8_t p_hi[2], p_lo[2], vf[16];
+      auto weight = [&](int r) { pw[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mref)); };
+      auto split_pair = [&](int r) {  // weights r, r+1 -> bf16 hi + lo operands
+        l_run += pw[r] + pw[r + 1];
+#pragma unroll
+        for (int e = r; e < r + 2; ++e) {
+          const __bf16 h = (__bf16)pw[e];
+          p_hi[e >> 3][e & 7] = h;
+          p_lo[e >> 3][e & 7] = kHiLo ? (__bf16)(pw[e] - (float)h) : (__bf16)0.f;
+        }
+      };
+
+      // scores of tile i+1; softmax of tile i behind them
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], sc, 0, 0, 0);
+        if (ks + kAhead < 18)
+          kf[ks + kAhead] = lds_b128(kbuf + k_frag_off<kDh>(kb, ks + kAhead));
+        else
+          vf[ks + kAhead - 18] = v_frag<kDh>(vbuf, pv_off_even, pv_off_odd, ks + kAhead - 18);
+        if (ks == 0) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) sv[r] = own[r] + part[r];
+        } else if (ks == 1) {
+#pragma unroll
+          for (int r = 8; r < 16; ++r) sv[r] = own[r] + part[r];
+        } else if (ks == 2) {
+          if (kMasked) {
+            // lane holds keys 8*(r>>2) + 4*half + (r&3) of the tile
+            const uint32_t lv = vis >> (4 * half);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!((lv >> (8 * (r >> 2) + (r & 3))) & 1u)) sv[r] = -INFINITY;
+          }
+          smax = sv[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) smax = fmax3(smax, sv[r]);
+        } else if (ks == 3) {
+          const float mt = partner_max(smax) * sl2;
+          m_seen = fmax3(m_seen, mt);
+          if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated for this head yet
+          ovf |= mt > m_ref + kRefHeadroom;
+          mref = m_ref == -INFINITY ? 0.f : m_ref;
+        } else if (ks == 4 || ks == 5) {
+          weight(4 * (ks - 4)); weight(4 * (ks - 4) + 1);
+          weight(4 * (ks - 4) + 2); weight(4 * (ks - 4) + 3);
+        } else if (ks == 6) {
+          split_pair(0);
+        } else if (ks == 7) {
+          weight(8); weight(9);
+        } else if (ks == 8) {
+          split_pair(2);
+        } else if (ks == 9) {
+          weight(10); weight(11);
+        } else if (ks == 10) {
+          split_pair(4);
+        } else if (ks == 11) {
+          split_pair(6);
+        } else if (ks == 12 || ks == 13) {
+          weight(2 * ks - 12); weight(2 * ks - 11);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // values of tile i: fragment j = dim block j&7, key step j>>3
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], p_hi[j >> 3], acc[j & 7], 0, 0, 0);
+        if (kHiLo)
+          acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], p_lo[j >> 3], acc[j & 7], 0, 0, 0);
+        if (j + kAhead < 16) vf[j + kAhead] = v_frag<kDh>(vbuf, pv_off_even, pv_off_odd, j + kAhead);
+        if (j < 4) {
+          split_pair(8 + 2 * j);
+        } else if (j < 8) {
+#pragma unroll
+          for (int r = 4 * (j - 4); r < 4 * (j - 3); ++r) dst[r * 64 + lane] = sc[r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      own = sc;
+    };
+
+    // Tile i+1 landed and tile i's partial scores are published once every
+    // wave passes the barrier; ring slot (i+2)%3 is free from then on.
+    auto advance = [&](int i) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of tile i+1 landed
+      __syncthreads();
       if (i + 2 < ntiles)
         issue_tile(lds + ((i + 2) % kRing) * kTileBytes, lat_rs, rope_rs, (i + 2) * kTile, wave,
                    lane, rope_voff);
-      // next tile's score MFMAs go first so that they overlap this tile's softmax
-      f32x16_t nxt;
-      if (i + 1 < ntiles) nxt = tile_scores<kDh>(lds + ((i + 1) % kRing) * kTileBytes, qreg, key, half);
-
-      const LDS_AS float* src = xs + ((i & 1) * 4 + partner) * 1024;
-      const int64_t key0 = c0 + (int64_t)i * kTile;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (own[r] + src[r * 64 + lane]) * a.scale_log2;
-      if (key0 + kTile > prefix || key0 + kTile > c1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t j = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (!key_visible(j, c1, prefix, anc)) x[r] = -INFINITY;
-        }
-      }
-      float mt = x[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmax3(mt, x[r]);
-      mt = partner_max(mt);
-      m_seen = fmax3(m_seen, mt);
-      if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated for this head yet
-      ovf |= mt > m_ref + kRefHeadroom;
-      const float mref = m_ref == -INFINITY ? 0.f : m_ref;
-
-      // softmax weights straight into the P^T operand layout
-      bf16x8_t p_hi[2], p_lo[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pw = __builtin_amdgcn_exp2f(x[r] - mref);
-        l_run += pw;
-        const __bf16 h = (__bf16)pw;
-        p_hi[r >> 3][r & 7] = h;
-        p_lo[r >> 3][r & 7] = kHiLo ? (__bf16)(pw - (float)h) : (__bf16)0.f;
-      }
-      tile_values<kDh, kHiLo>(acc, lds + (i % kRing) * kTileBytes, pv_off_even, pv_off_odd, p_hi, p_lo);
-
-      if (i + 1 < ntiles) {
-        LDS_AS float* dst = xs + (((i + 1) & 1) * 4 + wave) * 1024;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = nxt[r];
-        own = nxt;
-      }
+    };
+    // Tiles wholly inside the prefix and the chunk need no mask; the rest
+    // (tree keys, chunk tail) take the masked step in a loop of their own, so
+    // that each loop body has a single register assignment.
+    const int64_t full_end = prefix < c1 ? prefix : c1;
+    const int n_full = full_end > c0 ? (int)((full_end - c0) / kTile) : 0;
+    for (int i = 0; i < n_full; ++i) {
+      advance(i);
+      step(std::false_type{}, i, 0u);
+    }
+    for (int i = n_full; i < ntiles; ++i) {
+      advance(i);
+      step(std::true_type{}, i, tile_visibility(c0 + (int64_t)i * kTile, c1, prefix, anc));
     }
     if (!__syncthreads_or(ovf)) break;
     __syncthreads();
@@ -521,14 +640,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   const float* pl = a.part_lse + (int64_t)b * a.nsplit * rows_b + rb;
   const float* po = a.part_o + ((int64_t)b * a.nsplit * rows_b + rb) * kDl + 4 * d4;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) M = fmax3(M, pl[s * rows_b]);
   f32x4_t accv = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
+    // unrolled so that several partial loads are in flight per thread
+#pragma unroll 8
     for (int s = 0; s < ns; ++s) {
       const float w = __builtin_amdgcn_exp2f((pl[s * rows_b] - M) * kLog2e);
       wsum += w;
-      const f32x4_t o = *(const f32x4_t*)(po + s * rows_b * kDl);
+      const f32x4_t o = __builtin_nontemporal_load((const f32x4_t*)(po + s * rows_b * kDl));
       accv += w * o;
     }
   }
@@ -650,7 +772,7 @@ int common_checks(const void* qn, const void* qr, const void* lat, const void* r
   if (!aligned(qn, 16) || !aligned(qr, 16) || !aligned(lat, 16) || !aligned(rope, 16) ||
       !aligned(out, 16) || !aligned(lse, 4) || !aligned(parent, 4))
     return MLAV_ERR_ALIGN;
-  if (!std::isfinite(scale)) return MLAV_ERR_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return MLAV_ERR_ARG;
   return check_options(opt);
 }
 

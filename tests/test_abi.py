@@ -130,6 +130,8 @@ def test_host_validation_errors(lib):
         assert call(lib, **{k: A + 2}) == _lib.MLAV_ERR_ALIGN
     assert call(lib, scale=float("nan")) == _lib.MLAV_ERR_ARG
     assert call(lib, scale=float("inf")) == _lib.MLAV_ERR_ARG
+    assert call(lib, scale=0.0) == _lib.MLAV_ERR_ARG
+    assert call(lib, scale=-0.5) == _lib.MLAV_ERR_ARG
     bad = _lib.Options(0, 0, 0, 1)
     assert lib.mla_verify_ex(A, A, A, A, A, 100, 0.07, A, A, 9, 64, None, 0, None,
                              ctypes.byref(bad)) == _lib.MLAV_ERR_ARG
