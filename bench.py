@@ -149,28 +149,30 @@ def main() -> int:
     us_warm = timed(rotate=False)
     us_cold = timed(rotate=True)
 
-    # split kernel alone: events around each launch on the stream it runs on
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.warmup):
-        d = copies[i % ncopy]
+    # each kernel alone: K back-to-back launches (rotating inputs) between two
+    # events recorded on the stream the library launches on
+    def split(d):
         api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], p,
                                 case.scale, plan, part_out=d["po"], part_lse=d["pl"], pv_mode=args.pv_mode)
-        if plan.nsplit > 1:
-            api.combine(d["po"], d["pl"], out=d["out"].view(-1, 512), lse=d["lse"].view(-1))
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        d = copies[i % ncopy]
-        ev[i][0].record(stream)
-        api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], p,
-                                case.scale, plan, part_out=d["po"], part_lse=d["pl"], pv_mode=args.pv_mode)
-        ev[i][1].record(stream)
-        if plan.nsplit > 1:
-            api.combine(d["po"], d["pl"], out=d["out"].view(-1, 512), lse=d["lse"].view(-1))
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    split_us = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
-    combine_us = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+
+    def merge(d):
+        api.combine(d["po"], d["pl"], out=d["out"].view(-1, 512), lse=d["lse"].view(-1))
+
+    def batch_us(fn) -> float:
+        for i in range(args.warmup):
+            fn(copies[i % ncopy])
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(copies[i % ncopy])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    split_us = batch_us(split)
+    combine_us = batch_us(merge) if plan.nsplit > 1 else 0.0
 
     if args.copy_calib_mb > 0:
         nb = int(args.copy_calib_mb * 2**20) // 4 * 4
