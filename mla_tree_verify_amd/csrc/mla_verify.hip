@@ -63,8 +63,12 @@ constexpr int kLatBytes = kTile * kDl * 2;       // 32768
 constexpr int kRopeBytes = kTile * kDr * 2;      // 4096
 constexpr int kTileBytes = kLatBytes + kRopeBytes;  // 36864
 constexpr int kRing = 3;                         // tiles in flight
-constexpr int kLdsBytes = kRing * kTileBytes + 2 * 4 * 16 * 64 * 4;  // + score exchange = 143360
+constexpr int kXsBytes = 2 * 4 * 16 * 64 * 4;  // score exchange: [2][4 waves][16][64] fp32
+constexpr int kLdsBytes = kRing * kTileBytes + kXsBytes;  // 143360
+constexpr int kStageHeads = kTileBytes / (kDl * 4);  // 18 output rows staged per ring slot
 constexpr int kThreads = 256;
+static_assert(kRing * kStageHeads + kXsBytes / (kDl * 4) >= kHeads,
+              "the epilogue stages a token's 64 x 512 fp32 outputs in the ring slots and the exchange buffer");
 constexpr int kXcds = 8;
 constexpr int64_t kChunkGran = kTile;
 constexpr int64_t kMinChunk = 128;
@@ -76,6 +80,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 struct Args {
   const uint16_t* qn;    // [B, q, H, 512]
@@ -209,23 +215,32 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Issue this wave's quarter of the direct-to-LDS loads of one 32-key tile.
+// Issue this wave's quarter of the direct-to-LDS loads of one 32-key tile
+// (issue_tile_part: load `part` of the nine).
 // key_rel = first key of the tile relative to the descriptors' first row.
 // Latent row k lands at buf + 1024 k with its 16-byte chunks XOR-swizzled by
 // swz(k); the rope rows follow the 32 latent rows, 128 B each, swizzled alike.
+__device__ inline void issue_tile_part(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_rs,
+                                       __amdgpu_buffer_rsrc_t rope_rs, int key_rel, int wave, int lane,
+                                       int rope_voff, int part) {
+  // The whole byte offset goes in the VGPR operand: raw-buffer range checks
+  // cover the VGPR offset (plus the immediate) but not the SGPR offset.
+  if (part < 8) {
+    const int k = 4 * part + wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rs, (LDS_AS void*)(buf + k * 1024), 16,
+                                             (key_rel + k) * 1024 + 16 * (lane ^ swz(k)), 0, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rs, (LDS_AS void*)(buf + kLatBytes + wave * 1024), 16,
+                                             (key_rel + 8 * wave) * 128 + rope_voff, 0, 0, 0);
+  }
+}
+
 __device__ inline void issue_tile(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_rs,
                                   __amdgpu_buffer_rsrc_t rope_rs, int key_rel, int wave, int lane,
                                   int rope_voff) {
-  // The whole byte offset goes in the VGPR operand: raw-buffer range checks
-  // cover the VGPR offset (plus the immediate) but not the SGPR offset.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k = 4 * i + wave;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rs, (LDS_AS void*)(buf + k * 1024), 16,
-                                             (key_rel + k) * 1024 + 16 * (lane ^ swz(k)), 0, 0, 0);
-  }
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rs, (LDS_AS void*)(buf + kLatBytes + wave * 1024), 16,
-                                           (key_rel + 8 * wave) * 128 + rope_voff, 0, 0, 0);
+  for (int part = 0; part < 9; ++part)
+    issue_tile_part(buf, lat_rs, rope_rs, key_rel, wave, lane, rope_voff, part);
 }
 
 // Lane bases of the K operand reads. Score k-step ks of a wave reads 16-byte
@@ -261,15 +276,11 @@ __device__ inline int k_frag_off(const KBases& kb, int ks) {
 
 __device__ inline bf16x8_t lds_b128(const LDS_AS char* p) { return *(const LDS_AS bf16x8_t*)p; }
 
-// V^T operand of value fragment j (dim block j&7 of this wave's 256 dims, key
-// step j>>3), read from the latent rows with two transposing LDS reads.
-template <int kDh>
-__device__ inline bf16x8_t v_frag(const LDS_AS char* buf, int pv_off_even, int pv_off_odd, int j) {
-  const int dbg = 8 * kDh + (j & 7);
-  const int base = ((dbg & 1) ? pv_off_odd : pv_off_even) + 128 * (dbg >> 1) + 16 * 1024 * (j >> 3);
-  const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(buf + base));
-  const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(buf + base + 8 * 1024));
-  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+// Returns x unchanged but opaque to the optimiser, so that an address formed
+// once per loop iteration is not split into one hoisted register per use.
+__device__ inline int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // Partial scores of one tile over this wave's half of the 576 dims:
@@ -290,9 +301,13 @@ __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&
 // partial scores over their dim half, swap them through LDS and end up with
 // identical full scores, softmax weights and denominators; each then owns
 // 256 of the 512 output dims.
+// The three ring slots and the exchange buffer are separate LDS objects: the
+// compiler can then tell that a tile load into one slot does not write the
+// slots being read, and issues no wait for the load before those reads.
 template <int kDh, bool kHiLo>
-__device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s, int t, int wave,
-                                  int hh, int lane, int64_t row0, int64_t n) {
+__device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r1, LDS_AS char* r2,
+                                  LDS_AS float* xs, int b, int s, int t, int wave, int hh, int lane,
+                                  int64_t row0, int64_t n) {
   const int half = lane >> 5;
   const int64_t prefix = n - a.q;
   const int64_t c0 = (int64_t)s * a.chunk;
@@ -330,7 +345,8 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
       make_rsrc(a.rope + (row0 + c0) * kDr, (uint32_t)((n - c0) * kDr * 2));
   const int rope_voff = (lane >> 3) * 128 + 16 * ((lane & 7) ^ swz(lane >> 3));
 
-  LDS_AS float* xs = (LDS_AS float*)(lds + kRing * kTileBytes);  // [2][4 waves][16][64]
+  // ring slot r (a compile-time r selects the object itself)
+  auto ring = [&](int r) { return r == 0 ? r0 : (r == 1 ? r1 : r2); };
   const int partner = wave ^ 1;  // same head half, other dim half
   const KBases kb = make_kbases(lane & 31, half);
 
@@ -352,11 +368,11 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
     int ovf = 0;
 
     // prologue: tiles 0 and 1 in flight, partial scores of tile 0 published
-    issue_tile(lds, lat_rs, rope_rs, 0, wave, lane, rope_voff);
-    if (ntiles > 1) issue_tile(lds + kTileBytes, lat_rs, rope_rs, kTile, wave, lane, rope_voff);
+    issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+    if (ntiles > 1) issue_tile(r1, lat_rs, rope_rs, kTile, wave, lane, rope_voff);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    f32x16_t own = tile_scores<kDh>(lds, qreg, kb);
+    f32x16_t own = tile_scores<kDh>(r0, qreg, kb);
     {
       LDS_AS float* dst = xs + (0 * 4 + wave) * 1024;
 #pragma unroll
@@ -365,40 +381,64 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
 
     // One step: softmax and values of tile i, scores of tile i+1 (computed
     // even past the last tile, on whatever that ring slot holds, and unused
-    // then). The body is an explicit software pipeline over MFMA slots: each
-    // LDS operand is read four MFMAs before its use, and the softmax
-    // arithmetic is cut into slices of about one MFMA's duration that issue
-    // behind the MFMAs. sched_barrier fences keep the slots in this order.
-    // kMasked selects the per-key visibility test.
-    auto step = [&](auto masked_tag, int i, uint32_t vis) {
+    // then), and the loads of tile i+2 into the free ring slot, spread over
+    // the score MFMA slots (issuing the nine loads back to back stalls the
+    // wave for several hundred cycles). The body is an explicit software pipeline over MFMA slots: each
+    // LDS operand is read kAhead MFMA slots before its use (with four waves
+    // the LDS needs about eight reads in flight per wave to approach its
+    // bandwidth), and the softmax arithmetic is cut into slices of about one
+    // MFMA's duration that issue behind the MFMAs. sched_barrier fences keep
+    // the slots in this order. kMasked selects the per-key visibility test.
+    auto step = [&](auto masked_tag, LDS_AS char* kbuf, LDS_AS char* vbuf, LDS_AS char* dma_buf, int i,
+                    uint32_t vis) {
       constexpr bool kMasked = decltype(masked_tag)::value;
-      constexpr int kAhead = 4;
-      const LDS_AS char* kbuf = lds + ((i + 1) % kRing) * kTileBytes;
-      const LDS_AS char* vbuf = lds + (i % kRing) * kTileBytes;
+      const bool dma = i + 2 < ntiles;
+      constexpr int kAhead = 8;
+      auto kread = [&](int ks) {
+        const int c0 = 36 * kDh + 2 * ks;  // even chunk of the 576-d row
+        return lds_b128(kbuf + (c0 < 64 ? kb.lat[(c0 & 7) >> 1] + 16 * (c0 & ~7) : kb.rope[((c0 - 64) & 7) >> 1]));
+      };
+      auto vread = [&](int j) {  // dim block j&7 of this wave's 256 dims, key step j>>3
+        const int dbg = 8 * kDh + (j & 7);
+        const int off = ((dbg & 1) ? pv_off_odd : pv_off_even) + 128 * (dbg >> 1) + 16 * 1024 * (j >> 3);
+        const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(vbuf + off));
+        const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(vbuf + off + 8 * 1024));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
       const LDS_AS float* src = xs + ((i & 1) * 4 + partner) * 1024;
       LDS_AS float* dst = xs + (((i + 1) & 1) * 4 + wave) * 1024;
 
       float part[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) part[r] = src[r * 64 + lane];
-      bf16x8_t kf[18];
-#pragma unroll
-      for (int ks = 0; ks < kAhead; ++ks) kf[ks] = lds_b128(kbuf + k_frag_off<kDh>(kb, ks));
       __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t kf[18], vf[16];
+#pragma unroll
+      for (int ks = 0; ks < kAhead; ++ks) {
+        kf[ks] = kread(ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 
       f32x16_t sc = {};
       float sv[16], pw[16];
       float smax = 0.f, mref = 0.f;
-      bf16x8_t p_hi[2], p_lo[2], vf[16];
+      u32x4_t ph[2], pl[2];  // bf16 pairs of the P^T operand (hi and lo parts)
       auto weight = [&](int r) { pw[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mref)); };
-      auto split_pair = [&](int r) {  // weights r, r+1 -> bf16 hi + lo operands
+      // weights r, r+1 -> operand words: hi = the weight rounded to bf16,
+      // lo = the exact remainder rounded to bf16, so that hi + lo carries
+      // about 17 significant bits.
+      auto split_pair = [&](int r) {
         l_run += pw[r] + pw[r + 1];
-#pragma unroll
-        for (int e = r; e < r + 2; ++e) {
-          const __bf16 h = (__bf16)pw[e];
-          p_hi[e >> 3][e & 7] = h;
-          p_lo[e >> 3][e & 7] = kHiLo ? (__bf16)(pw[e] - (float)h) : (__bf16)0.f;
+        const bf16x2_t h2 = {(__bf16)pw[r], (__bf16)pw[r + 1]};
+        const uint32_t hi = __builtin_bit_cast(uint32_t, h2);
+        uint32_t lo = 0;
+        if (kHiLo) {
+          const bf16x2_t l2 = {(__bf16)(pw[r] - __uint_as_float(hi << 16)),
+                               (__bf16)(pw[r + 1] - __uint_as_float(hi & 0xffff0000u))};
+          lo = __builtin_bit_cast(uint32_t, l2);
         }
+        ph[r >> 3][(r & 7) >> 1] = hi;
+        pl[r >> 3][(r & 7) >> 1] = lo;
       };
 
       // scores of tile i+1; softmax of tile i behind them
@@ -406,9 +446,9 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
       for (int ks = 0; ks < 18; ++ks) {
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], sc, 0, 0, 0);
         if (ks + kAhead < 18)
-          kf[ks + kAhead] = lds_b128(kbuf + k_frag_off<kDh>(kb, ks + kAhead));
+          kf[ks + kAhead] = kread(ks + kAhead);
         else
-          vf[ks + kAhead - 18] = v_frag<kDh>(vbuf, pv_off_even, pv_off_odd, ks + kAhead - 18);
+          vf[ks + kAhead - 18] = vread(ks + kAhead - 18);
         if (ks == 0) {
 #pragma unroll
           for (int r = 0; r < 8; ++r) sv[r] = own[r] + part[r];
@@ -433,38 +473,43 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
           ovf |= mt > m_ref + kRefHeadroom;
           mref = m_ref == -INFINITY ? 0.f : m_ref;
         } else if (ks == 4 || ks == 5) {
-          weight(4 * (ks - 4)); weight(4 * (ks - 4) + 1);
-          weight(4 * (ks - 4) + 2); weight(4 * (ks - 4) + 3);
+          weight(2 * (ks - 4)); weight(2 * (ks - 4) + 1);
         } else if (ks == 6) {
           split_pair(0);
         } else if (ks == 7) {
-          weight(8); weight(9);
+          weight(4); weight(5);
         } else if (ks == 8) {
           split_pair(2);
         } else if (ks == 9) {
-          weight(10); weight(11);
+          weight(6); weight(7);
         } else if (ks == 10) {
           split_pair(4);
-        } else if (ks == 11) {
+        } else if (ks == 12) {
           split_pair(6);
-        } else if (ks == 12 || ks == 13) {
-          weight(2 * ks - 12); weight(2 * ks - 11);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // values of tile i: fragment j = dim block j&7, key step j>>3
+      // values of tile i: fragment j = dim block j&7, key step j>>3. Each slot
+      // holds two MFMAs, so the second half of the softmax, the loads of tile
+      // i+2 and the publication of tile i+1's partial scores go here.
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], p_hi[j >> 3], acc[j & 7], 0, 0, 0);
+        acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], __builtin_bit_cast(bf16x8_t, ph[j >> 3]),
+                                                             acc[j & 7], 0, 0, 0);
         if (kHiLo)
-          acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], p_lo[j >> 3], acc[j & 7], 0, 0, 0);
-        if (j + kAhead < 16) vf[j + kAhead] = v_frag<kDh>(vbuf, pv_off_even, pv_off_odd, j + kAhead);
+          acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], __builtin_bit_cast(bf16x8_t, pl[j >> 3]),
+                                                               acc[j & 7], 0, 0, 0);
+        if (j + kAhead < 16) vf[j + kAhead] = vread(j + kAhead);
+        if (j < 9 && dma)
+          issue_tile_part(dma_buf, lat_rs, rope_rs, (i + 2) * kTile, wave, lane, rope_voff, j);
         if (j < 4) {
-          split_pair(8 + 2 * j);
+          weight(8 + 2 * j); weight(9 + 2 * j);
         } else if (j < 8) {
+          split_pair(8 + 2 * (j - 4));
+        } else if (j < 12) {
 #pragma unroll
-          for (int r = 4 * (j - 4); r < 4 * (j - 3); ++r) dst[r * 64 + lane] = sc[r];
+          for (int r = 4 * (j - 8); r < 4 * (j - 7); ++r) dst[r * 64 + lane] = sc[r];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -473,52 +518,80 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
 
     // Tile i+1 landed and tile i's partial scores are published once every
     // wave passes the barrier; ring slot (i+2)%3 is free from then on.
-    auto advance = [&](int i) {
+    auto advance = [&]() {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of tile i+1 landed
       __syncthreads();
-      if (i + 2 < ntiles)
-        issue_tile(lds + ((i + 2) % kRing) * kTileBytes, lat_rs, rope_rs, (i + 2) * kTile, wave,
-                   lane, rope_voff);
     };
     // Tiles wholly inside the prefix and the chunk need no mask; the rest
     // (tree keys, chunk tail) take the masked step in a loop of their own, so
     // that each loop body has a single register assignment.
+    // The unmasked loop is unrolled by the ring period so that every step's
+    // slots are compile-time objects; the remaining tiles (fewer than three
+    // unmasked ones, then the masked ones) take the masked step with the
+    // slots chosen at run time.
     const int64_t full_end = prefix < c1 ? prefix : c1;
     const int n_full = full_end > c0 ? (int)((full_end - c0) / kTile) : 0;
-    for (int i = 0; i < n_full; ++i) {
-      advance(i);
-      step(std::false_type{}, i, 0u);
+    int i = 0;
+    for (; i + 3 <= n_full; i += 3) {
+      advance();
+      step(std::false_type{}, r1, r0, r2, i, 0u);
+      advance();
+      step(std::false_type{}, r2, r1, r0, i + 1, 0u);
+      advance();
+      step(std::false_type{}, r0, r2, r1, i + 2, 0u);
     }
-    for (int i = n_full; i < ntiles; ++i) {
-      advance(i);
-      step(std::true_type{}, i, tile_visibility(c0 + (int64_t)i * kTile, c1, prefix, anc));
+    for (; i < ntiles; ++i) {
+      advance();
+      step(std::true_type{}, ring((i + 1) % kRing), ring(i % kRing), ring((i + 2) % kRing), i,
+           tile_visibility(c0 + (int64_t)i * kTile, c1, prefix, anc));
     }
     if (!__syncthreads_or(ovf)) break;
     __syncthreads();
   }
 
-  // normalise and store this wave's 32 heads x 256 dims
+  // Normalise, then store through LDS (free now: no tile load is in flight
+  // after the last step) so that each global store instruction writes 1 KB of
+  // one head's row instead of 32-byte pieces of 32 rows. Staging layout: head
+  // h's row in LDS object h / 18 (ring slots 0..2, then the exchange buffer)
+  // at (h % 18) * 2048, its 128 16-byte chunks at 16 * (c ^ (h & 7)),
+  // conflict-free for both the column-wise writes and the row-wise reads.
+  auto stage_row = [&](int h) {
+    const int o = h / kStageHeads;
+    LDS_AS char* base = o == 0 ? r0 : (o == 1 ? r1 : (o == 2 ? r2 : (LDS_AS char*)xs));
+    return base + (h - o * kStageHeads) * (kDl * 4);
+  };
   const float l_tot = partner_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_val = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   const bool final_write = nsplit_b == 1;
-  const int64_t qrow = ((int64_t)b * a.q + t) * kHeads + head;
-  float* orow = final_write
-                    ? a.out + qrow * kDl
-                    : a.part_o + ((((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head) * kDl;
+  {
+    const int h = head;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < 8; ++db) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4_t v;
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t v;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = acc[db][4 * g + c] * inv;
-      *(f32x4_t*)(orow + 256 * kDh + 32 * db + 8 * g + 4 * half) = v;
+        for (int c = 0; c < 4; ++c) v[c] = acc[db][4 * g + c] * inv;
+        const int chunk = 64 * kDh + 8 * db + 2 * g + half;  // dims 4 chunk .. 4 chunk + 3
+        *(LDS_AS f32x4_t*)(stage_row(h) + 16 * (chunk ^ (h & 7))) = v;
+      }
     }
+  }
+  __syncthreads();
+  const int64_t row_t = (int64_t)b * a.q + t;
+  float* obase = final_write ? a.out + row_t * kHeads * kDl
+                             : a.part_o + (((int64_t)b * a.nsplit + s) * a.q + t) * kHeads * kDl;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int h = 16 * wave + (k >> 1);
+    const int chunk = 64 * (k & 1) + lane;
+    const f32x4_t v = *(const LDS_AS f32x4_t*)(stage_row(h) + 16 * (chunk ^ (h & 7)));
+    *(f32x4_t*)(obase + (int64_t)h * kDl + 4 * chunk) = v;
   }
   if (kDh == 0 && half == 0) {
     if (final_write)
-      a.lse[qrow] = lse_val;
+      a.lse[row_t * kHeads + head] = lse_val;
     else
       a.part_lse[(((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head] = lse_val;
   }
@@ -527,8 +600,14 @@ __device__ inline void split_body(const Args& a, LDS_AS char* lds, int b, int s,
 template <bool kHiLo>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_mfma_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) char lds_raw[kLdsBytes];
-  LDS_AS char* lds = (LDS_AS char*)lds_raw;
+  __shared__ __attribute__((aligned(16))) char ring0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char ring1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char ring2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) float xs[kXsBytes / 4];
+  LDS_AS char* r0 = (LDS_AS char*)ring0;
+  LDS_AS char* r1 = (LDS_AS char*)ring1;
+  LDS_AS char* r2 = (LDS_AS char*)ring2;
+  LDS_AS float* x = (LDS_AS float*)xs;
   int b, s, t;
   if (!decode_work(a, b, s, t)) return;
   const int tid = threadIdx.x;
@@ -544,9 +623,9 @@ void split_mfma_kernel(Args a) {
   if ((int64_t)s * a.chunk >= n) return;  // this sequence needs fewer splits
   const int hh = wave >> 1;
   if ((wave & 1) == 0)
-    split_body<0, kHiLo>(a, lds, b, s, t, wave, hh, lane, row0, n);
+    split_body<0, kHiLo>(a, r0, r1, r2, x, b, s, t, wave, hh, lane, row0, n);
   else
-    split_body<1, kHiLo>(a, lds, b, s, t, wave, hh, lane, row0, n);
+    split_body<1, kHiLo>(a, r0, r1, r2, x, b, s, t, wave, hh, lane, row0, n);
 }
 
 // ---------------------------------------------------------------------------
