@@ -62,13 +62,13 @@ constexpr int kTile = 32;                        // keys per wave tile
 constexpr int kLatBytes = kTile * kDl * 2;       // 32768
 constexpr int kRopeBytes = kTile * kDr * 2;      // 4096
 constexpr int kTileBytes = kLatBytes + kRopeBytes;  // 36864
-constexpr int kRing = 3;                         // tiles in flight
-constexpr int kXsBytes = 2 * 4 * 16 * 64 * 4;  // score exchange: [2][4 waves][16][64] fp32
-constexpr int kLdsBytes = kRing * kTileBytes + kXsBytes;  // 143360
+constexpr int kRing = 4;                         // tile slots: values, scores, two loading
+constexpr int kXchgBytes = 4 * 2 * 64 * 16;      // one exchange area: [4 waves][2 chunks][64 lanes][16 B]
+constexpr int kLdsBytes = kRing * kTileBytes + 2 * kXchgBytes;  // 163840 = all of a CU's LDS
 constexpr int kStageHeads = kTileBytes / (kDl * 4);  // 18 output rows staged per ring slot
 constexpr int kThreads = 256;
-static_assert(kRing * kStageHeads + kXsBytes / (kDl * 4) >= kHeads,
-              "the epilogue stages a token's 64 x 512 fp32 outputs in the ring slots and the exchange buffer");
+static_assert(kRing * kStageHeads >= kHeads, "the epilogue stages a token's 64 x 512 fp32 outputs in the ring");
+static_assert(kLdsBytes <= 163840, "LDS per workgroup");
 constexpr int kXcds = 8;
 constexpr int64_t kChunkGran = kTile;
 constexpr int64_t kMinChunk = 128;
@@ -163,8 +163,16 @@ __device__ inline uint32_t tile_visibility(int64_t key0, int64_t c1, int64_t pre
   return m;
 }
 
-// Logical <-> physical 16-byte chunk swizzle inside a key row (low 3 bits only).
-__device__ inline int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
+// Logical <-> physical 16-byte chunk swizzles (XOR on the chunk index).
+// Latent rows (64 chunks): the low 4 bits. The LDS has 64 four-byte banks,
+// i.e. 16 chunk positions: the 128-bit score-operand reads of 16 consecutive
+// keys at one logical chunk then hit 16 different positions, and the
+// transposing value-operand reads (4 consecutive keys x 2 adjacent chunks
+// per 16 lanes) hit 8 different pairs.
+__device__ inline int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+// Rope rows (8 chunks, 128 B, two rows per 16 positions): 16 consecutive keys
+// at one logical chunk hit 16 different positions.
+__device__ inline int swz_rope(int k) { return (k >> 1) & 7; }
 
 __device__ inline float fmax3(float a, float b) { return __builtin_fmaxf(a, b); }
 
@@ -219,7 +227,8 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // (issue_tile_part: load `part` of the nine).
 // key_rel = first key of the tile relative to the descriptors' first row.
 // Latent row k lands at buf + 1024 k with its 16-byte chunks XOR-swizzled by
-// swz(k); the rope rows follow the 32 latent rows, 128 B each, swizzled alike.
+// swz(k); the rope rows follow the 32 latent rows, 128 B each, swizzled by
+// swz_rope(k).
 __device__ inline void issue_tile_part(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_rs,
                                        __amdgpu_buffer_rsrc_t rope_rs, int key_rel, int wave, int lane,
                                        int rope_voff, int part) {
@@ -245,24 +254,25 @@ __device__ inline void issue_tile(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_r
 
 // Lane bases of the K operand reads. Score k-step ks of a wave reads 16-byte
 // chunk c = 36 kDh + 2 ks + (lane>>5) of key lane&31's 576-d row (chunks
-// 0..63 latent, 64..71 rope), stored at chunk position c ^ swz(key) (low 3
-// bits). Since 36 kDh + 2 ks is even, that position is
-// (c & ~7) | (e2 ^ hs) with e2 = (36 kDh + 2 ks) & 7 and hs = (lane>>5) ^ swz(key),
-// so four per-lane bases (one per e2) plus a compile-time offset cover all
-// k-steps.
+// 0..63 latent, 64..71 rope). A latent chunk is stored at position
+// (c & ~15) | ((c & 15) ^ swz(key)); since 36 kDh + 2 ks is even, that is
+// (c & ~15) | (e2 ^ hs) with e2 = (36 kDh + 2 ks) & 15 and
+// hs = (lane>>5) ^ swz(key), so eight per-lane bases (one per e2) plus a
+// compile-time offset cover the latent k-steps; rope chunk c - 64 is at
+// position (c - 64) ^ swz_rope(key), four bases.
 struct KBases {
-  int lat[4];   // key * 1024 + 16 * ((2e) ^ hs)
-  int rope[4];  // kLatBytes + key * 128 + 16 * ((2e) ^ hs)
+  int lat[8];   // key * 1024 + 16 * ((2e) ^ hs)
+  int rope[4];  // kLatBytes + key * 128 + 16 * ((2e) ^ ((lane>>5) ^ swz_rope(key)))
 };
 
 __device__ inline KBases make_kbases(int key, int half) {
   KBases kb;
   const int hs = half ^ swz(key);
+  const int hr = half ^ swz_rope(key);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    kb.lat[e] = key * 1024 + 16 * ((2 * e) ^ hs);
-    kb.rope[e] = kLatBytes + key * 128 + 16 * ((2 * e) ^ hs);
-  }
+  for (int e = 0; e < 8; ++e) kb.lat[e] = key * 1024 + 16 * ((2 * e) ^ hs);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) kb.rope[e] = kLatBytes + key * 128 + 16 * ((2 * e) ^ hr);
   return kb;
 }
 
@@ -270,8 +280,8 @@ __device__ inline KBases make_kbases(int key, int half) {
 template <int kDh>
 __device__ inline int k_frag_off(const KBases& kb, int ks) {
   const int c0 = 36 * kDh + 2 * ks;  // even chunk index of the pair
-  if (c0 < 64) return kb.lat[(c0 & 7) >> 1] + 16 * (c0 & ~7);
-  return kb.rope[((c0 - 64) & 7) >> 1];
+  if (c0 < 64) return kb.lat[(c0 & 15) >> 1] + 16 * (c0 & ~15);
+  return kb.rope[(c0 - 64) >> 1];
 }
 
 __device__ inline bf16x8_t lds_b128(const LDS_AS char* p) { return *(const LDS_AS bf16x8_t*)p; }
@@ -298,16 +308,24 @@ __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&
 
 // One workgroup = one draft token x 64 heads x one KV chunk; 4 waves =
 // 2 head halves (hh) x 2 dim halves (kDh). Both waves of a head half compute
-// partial scores over their dim half, swap them through LDS and end up with
-// identical full scores, softmax weights and denominators; each then owns
-// 256 of the 512 output dims.
-// The three ring slots and the exchange buffer are separate LDS objects: the
-// compiler can then tell that a tile load into one slot does not write the
-// slots being read, and issues no wait for the load before those reads.
+// partial scores of every tile over their dim half. The softmax is split
+// between them: the wave with dim half kDh owns the tile's keys
+// [16 kDh, 16 kDh + 16) (accumulator elements r = 8 kDh .. 8 kDh + 7), so
+// each wave sends its partner the partial scores of the partner's keys,
+// turns the full scores of its own keys into bf16 hi + lo weights, and the
+// two swap those weights. Each wave then accumulates 256 of the 512 output
+// dims over all 32 keys.
+//
+// LDS: four ring slots (separate objects, so the compiler can see that a
+// tile load into one slot does not write the slots being read and issues no
+// wait for it), an 8 KB partial-score exchange and an 8 KB weight exchange:
+// 163840 bytes. A tile is loaded three steps ahead of its value product.
 template <int kDh, bool kHiLo>
 __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r1, LDS_AS char* r2,
-                                  LDS_AS float* xs, int b, int s, int t, int wave, int hh, int lane,
-                                  int64_t row0, int64_t n) {
+                                  LDS_AS char* r3, LDS_AS char* xs, LDS_AS char* xp, int b, int s,
+                                  int t, int wave, int hh, int lane, int64_t row0, int64_t n) {
+  constexpr int kOwn = 8 * kDh;         // this wave's softmax elements
+  constexpr int kSend = 8 * (1 - kDh);  // the partner's
   const int half = lane >> 5;
   const int64_t prefix = n - a.q;
   const int64_t c0 = (int64_t)s * a.chunk;
@@ -328,14 +346,20 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     }
   }
 
-  int pv_off_even, pv_off_odd;
+  // V^T operand (transposing reads): in each 16-lane group lane i reads 4
+  // dims (16 dhalf + 4 (i&3) ..) of key row kk = 4 half + (i>>2) (+8 v for
+  // the second read, +16 per key step); chunk 4 db + 2 dhalf + ((i&3)>>1) of
+  // dim block db. Under swz(kk) the low chunk bits become
+  // z0 ^ 4 (db & 1) ^ 8 (((db >> 1) ^ v) & 1), with z0 below, and db >> 2
+  // adds 16 chunks: four per-lane bases vb[m], m = (db & 1) + 2 (((db >> 1) ^ v) & 1).
+  int vb[4];
   {
     const int i = lane & 15;
     const int dhalf = (lane >> 4) & 1;
     const int kk = 4 * half + (i >> 2);
-    const int z = (2 * dhalf + ((i & 3) >> 1)) ^ (((i >> 2) << 1) | half);
-    pv_off_even = kk * 1024 + 16 * z + 8 * (i & 1);
-    pv_off_odd = kk * 1024 + 16 * (z ^ 4) + 8 * (i & 1);
+    const int z0 = (2 * dhalf + ((i & 3) >> 1)) ^ (((i >> 2) << 1) | half);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) vb[m] = kk * 1024 + 16 * (z0 ^ (4 * m)) + 8 * (i & 1);
   }
 
   const int ntiles = (int)((c1 - c0 + kTile - 1) / kTile);
@@ -343,74 +367,115 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       make_rsrc(a.lat + (row0 + c0) * kDl, (uint32_t)((n - c0) * kDl * 2));
   const __amdgpu_buffer_rsrc_t rope_rs =
       make_rsrc(a.rope + (row0 + c0) * kDr, (uint32_t)((n - c0) * kDr * 2));
-  const int rope_voff = (lane >> 3) * 128 + 16 * ((lane & 7) ^ swz(lane >> 3));
+  // rope row 8 wave + (lane>>3) of a tile: LDS position lane&7 holds
+  // logical chunk (lane&7) ^ swz_rope(row)
+  const int rope_voff = (lane >> 3) * 128 + 16 * ((lane & 7) ^ swz_rope(8 * wave + (lane >> 3)));
 
-  // ring slot r (a compile-time r selects the object itself)
-  auto ring = [&](int r) { return r == 0 ? r0 : (r == 1 ? r1 : r2); };
   const int partner = wave ^ 1;  // same head half, other dim half
   const KBases kb = make_kbases(lane & 31, half);
+  // exchange areas: [wave][chunk][lane][16 B], 2 KB per wave
+  LDS_AS char* xs_mine = xs + wave * 2048 + lane * 16;
+  LDS_AS char* xs_part = xs + partner * 2048 + lane * 16;
+  LDS_AS char* xp_mine = xp + wave * 2048 + lane * 16;
+  LDS_AS char* xp_part = xp + partner * 2048 + lane * 16;
+  // ring slot r (a compile-time r selects the object itself)
+  auto ring = [&](int r) { return r == 0 ? r0 : (r == 1 ? r1 : (r == 2 ? r2 : r3)); };
+  // lane holds keys 8*(r>>2) + 4*half + (r&3) of a tile in accumulator element r
+  auto key_visible_bit = [&](uint32_t vis, int r) {
+    return ((vis >> (4 * half + 8 * (r >> 2) + (r & 3))) & 1u) != 0;
+  };
 
-  // Online softmax with a reference max that never moves inside the loop: the
-  // first visible tile fixes it, later weights are 2^(s - m_ref), exact for
-  // any m_ref. A score more than kRefHeadroom above m_ref could overflow; then
-  // the chunk is redone once with m_ref = the chunk's observed max, which no
-  // score exceeds. The accumulator is never rescaled inside the loop.
+  // Online softmax with a reference max that never moves inside the loop:
+  // the first tile with a visible key fixes it (the max of that tile's full
+  // scores, the same in all four waves), later weights are 2^(s - m_ref),
+  // exact for any m_ref. A score more than kRefHeadroom above m_ref could
+  // overflow; then the chunk is redone once with m_ref = the chunk's observed
+  // max, which no score exceeds. The accumulator is never rescaled.
   f32x16_t acc[8];
   float m_ref = -INFINITY;  // log2 units, this lane's head
-  float l_run = 0.f;        // this lane's share of the softmax denominator
-  float m_seen = -INFINITY;
+  float l_run = 0.f;        // this lane's share of the softmax denominator (own keys)
+  float m_seen = -INFINITY; // max over own keys
+  bool have_ref = false;    // uniform over the workgroup: a visible key has been seen
   const float sl2 = a.scale_log2;  // > 0, so max(s) * sl2 = max(s * sl2)
   for (int attempt = 0; attempt < 2; ++attempt) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[db] = (f32x16_t){};
     l_run = 0.f;
-    if (attempt == 1) m_ref = m_seen;
     int ovf = 0;
 
-    // prologue: tiles 0 and 1 in flight, partial scores of tile 0 published
+    // prologue: tiles 0..2 in flight; tile 0's partial scores exchanged in
+    // full (through ring slot 3, free until tile 3 is loaded) to fix m_ref,
+    // then its partner half published for step 0
     issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
     if (ntiles > 1) issue_tile(r1, lat_rs, rope_rs, kTile, wave, lane, rope_voff);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (ntiles > 2) issue_tile(r2, lat_rs, rope_rs, 2 * kTile, wave, lane, rope_voff);
+    if (ntiles > 2)
+      __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18): tile 0 landed
+    else if (ntiles > 1)
+      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     f32x16_t own = tile_scores<kDh>(r0, qreg, kb);
-    {
-      LDS_AS float* dst = xs + (0 * 4 + wave) * 1024;
+    if (attempt == 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = own[r];
+      for (int c = 0; c < 4; ++c)
+        *(LDS_AS f32x4_t*)(r3 + wave * 4096 + c * 1024 + lane * 16) =
+            (f32x4_t){own[4 * c], own[4 * c + 1], own[4 * c + 2], own[4 * c + 3]};
+      __syncthreads();
+      const uint32_t vis0 = tile_visibility(c0, c1, prefix, anc);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t p4 = *(const LDS_AS f32x4_t*)(r3 + partner * 4096 + c * 1024 + lane * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key_visible_bit(vis0, 4 * c + e)) mx = fmax3(mx, own[4 * c + e] + p4[e]);
+      }
+      have_ref = vis0 != 0;
+      m_ref = have_ref ? partner_max(mx) * sl2 : -INFINITY;
     }
+    *(LDS_AS f32x4_t*)(xs_mine) = (f32x4_t){own[kSend], own[kSend + 1], own[kSend + 2], own[kSend + 3]};
+    *(LDS_AS f32x4_t*)(xs_mine + 1024) =
+        (f32x4_t){own[kSend + 4], own[kSend + 5], own[kSend + 6], own[kSend + 7]};
 
-    // One step: softmax and values of tile i, scores of tile i+1 (computed
-    // even past the last tile, on whatever that ring slot holds, and unused
-    // then), and the loads of tile i+2 into the free ring slot, spread over
-    // the score MFMA slots (issuing the nine loads back to back stalls the
-    // wave for several hundred cycles). The body is an explicit software pipeline over MFMA slots: each
-    // LDS operand is read kAhead MFMA slots before its use (with four waves
-    // the LDS needs about eight reads in flight per wave to approach its
-    // bandwidth), and the softmax arithmetic is cut into slices of about one
-    // MFMA's duration that issue behind the MFMAs. sched_barrier fences keep
-    // the slots in this order. kMasked selects the per-key visibility test.
+    // One step: softmax (own keys) and values (all keys) of tile i, scores
+    // of tile i+1 (computed even past the last tile, on whatever that ring
+    // slot holds, and unused then), loads of tile i+3 into the free slot.
+    // The body is an explicit software pipeline over MFMA slots: each LDS
+    // operand is read kAhead slots before its use, and the softmax is cut
+    // into slices of about one MFMA's issue budget placed behind the score
+    // MFMAs (a wave issues one instruction per 4 cycles, eight per 32-cycle
+    // MFMA). sched_barrier fences keep the slots in this order. Between the
+    // score and the value phases the waves meet at a barrier, after which
+    // each reads its partner's weights. kMasked selects the per-key
+    // visibility test (and the first-visible-tile path).
     auto step = [&](auto masked_tag, LDS_AS char* kbuf, LDS_AS char* vbuf, LDS_AS char* dma_buf, int i,
                     uint32_t vis) {
       constexpr bool kMasked = decltype(masked_tag)::value;
-      const bool dma = i + 2 < ntiles;
       constexpr int kAhead = 8;
+      const bool dma = i + 3 < ntiles;
       auto kread = [&](int ks) {
-        const int c0 = 36 * kDh + 2 * ks;  // even chunk of the 576-d row
-        return lds_b128(kbuf + (c0 < 64 ? kb.lat[(c0 & 7) >> 1] + 16 * (c0 & ~7) : kb.rope[((c0 - 64) & 7) >> 1]));
+        const int cc = 36 * kDh + 2 * ks;  // even chunk of the 576-d row
+        return lds_b128(kbuf + k_frag_off<kDh>(kb, ks));
       };
+      // fragment order: the wave's own key step first (its weights are ready
+      // first), then the partner's
+      auto frag = [&](int nn) { return nn < 8 ? 8 * kDh + nn : 8 * (1 - kDh) + (nn - 8); };
       auto vread = [&](int j) {  // dim block j&7 of this wave's 256 dims, key step j>>3
         const int dbg = 8 * kDh + (j & 7);
-        const int off = ((dbg & 1) ? pv_off_odd : pv_off_even) + 128 * (dbg >> 1) + 16 * 1024 * (j >> 3);
-        const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(vbuf + off));
-        const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(vbuf + off + 8 * 1024));
+        const int off = 256 * (dbg >> 2) + 16 * 1024 * (j >> 3);
+        const int m0 = (dbg & 1) + 2 * ((dbg >> 1) & 1);  // keys +0..3 (v = 0)
+        const int m1 = m0 ^ 2;                             // keys +8..11 (v = 1)
+        const bf16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(vbuf + vb[m0] + off));
+        const bf16x4_t v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)(vbuf + vb[m1] + off + 8 * 1024));
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      const LDS_AS float* src = xs + ((i & 1) * 4 + partner) * 1024;
-      LDS_AS float* dst = xs + (((i + 1) & 1) * 4 + wave) * 1024;
 
-      float part[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part[r] = src[r * 64 + lane];
+      // the partner's partial scores of this wave's keys of tile i
+      const f32x4_t pa = *(const LDS_AS f32x4_t*)(xs_part);
+      const f32x4_t pb = *(const LDS_AS f32x4_t*)(xs_part + 1024);
       __builtin_amdgcn_sched_barrier(0);
       bf16x8_t kf[18], vf[16];
 #pragma unroll
@@ -420,147 +485,172 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       }
 
       f32x16_t sc = {};
-      float sv[16], pw[16];
+      float sv[8], pw[8];
       float smax = 0.f, mref = 0.f;
-      u32x4_t ph[2], pl[2];  // bf16 pairs of the P^T operand (hi and lo parts)
-      auto weight = [&](int r) { pw[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mref)); };
-      // weights r, r+1 -> operand words: hi = the weight rounded to bf16,
+      u32x4_t ph[2], pl[2];  // bf16 pairs of the P^T operand (hi and lo parts), per key step
+      auto weight = [&](int k) { pw[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[k], sl2, -mref)); };
+      // own weights k, k+1 -> operand words: hi = the weight rounded to bf16,
       // lo = the exact remainder rounded to bf16, so that hi + lo carries
       // about 17 significant bits.
-      auto split_pair = [&](int r) {
-        l_run += pw[r] + pw[r + 1];
-        const bf16x2_t h2 = {(__bf16)pw[r], (__bf16)pw[r + 1]};
+      auto split_pair = [&](int k) {
+        l_run += pw[k] + pw[k + 1];
+        const bf16x2_t h2 = {(__bf16)pw[k], (__bf16)pw[k + 1]};
         const uint32_t hi = __builtin_bit_cast(uint32_t, h2);
         uint32_t lo = 0;
         if (kHiLo) {
-          const bf16x2_t l2 = {(__bf16)(pw[r] - __uint_as_float(hi << 16)),
-                               (__bf16)(pw[r + 1] - __uint_as_float(hi & 0xffff0000u))};
+          const bf16x2_t l2 = {(__bf16)(pw[k] - __uint_as_float(hi << 16)),
+                               (__bf16)(pw[k + 1] - __uint_as_float(hi & 0xffff0000u))};
           lo = __builtin_bit_cast(uint32_t, l2);
         }
-        ph[r >> 3][(r & 7) >> 1] = hi;
-        pl[r >> 3][(r & 7) >> 1] = lo;
+        ph[kDh][k >> 1] = hi;
+        pl[kDh][k >> 1] = lo;
       };
 
-      // scores of tile i+1; softmax of tile i behind them
+      // scores of tile i+1; softmax of this wave's keys of tile i behind them
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qreg[ks], sc, 0, 0, 0);
         if (ks + kAhead < 18)
           kf[ks + kAhead] = kread(ks + kAhead);
         else
-          vf[ks + kAhead - 18] = vread(ks + kAhead - 18);
+          vf[frag(ks + kAhead - 18)] = vread(frag(ks + kAhead - 18));
         if (ks == 0) {
 #pragma unroll
-          for (int r = 0; r < 8; ++r) sv[r] = own[r] + part[r];
+          for (int k = 0; k < 4; ++k) sv[k] = own[kOwn + k] + pa[k];
         } else if (ks == 1) {
 #pragma unroll
-          for (int r = 8; r < 16; ++r) sv[r] = own[r] + part[r];
+          for (int k = 0; k < 4; ++k) sv[4 + k] = own[kOwn + 4 + k] + pb[k];
         } else if (ks == 2) {
           if (kMasked) {
-            // lane holds keys 8*(r>>2) + 4*half + (r&3) of the tile
-            const uint32_t lv = vis >> (4 * half);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (!((lv >> (8 * (r >> 2) + (r & 3))) & 1u)) sv[r] = -INFINITY;
+            for (int k = 0; k < 8; ++k)
+              if (!key_visible_bit(vis, kOwn + k)) sv[k] = -INFINITY;
           }
           smax = sv[0];
 #pragma unroll
-          for (int r = 1; r < 16; ++r) smax = fmax3(smax, sv[r]);
+          for (int k = 1; k < 8; ++k) smax = fmax3(smax, sv[k]);
         } else if (ks == 3) {
-          const float mt = partner_max(smax) * sl2;
+          const float mt = partner_max(smax) * sl2;  // max over this wave's 16 keys
           m_seen = fmax3(m_seen, mt);
-          if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated for this head yet
+          if (kMasked && !have_ref && vis != 0) {
+            // first tile with a visible key: both halves' maxes fix m_ref
+            // (uniform over the workgroup: visibility is per token)
+            __syncthreads();  // every wave has consumed its partner's scores
+            *(LDS_AS float*)(xs + wave * 2048 + lane * 4) = mt;
+            __syncthreads();
+            m_ref = fmax3(mt, *(const LDS_AS float*)(xs + partner * 2048 + lane * 4));
+            have_ref = true;
+          }
           ovf |= mt > m_ref + kRefHeadroom;
           mref = m_ref == -INFINITY ? 0.f : m_ref;
-        } else if (ks == 4 || ks == 5) {
-          weight(2 * (ks - 4)); weight(2 * (ks - 4) + 1);
-        } else if (ks == 6) {
-          split_pair(0);
-        } else if (ks == 7) {
-          weight(4); weight(5);
-        } else if (ks == 8) {
-          split_pair(2);
-        } else if (ks == 9) {
-          weight(6); weight(7);
-        } else if (ks == 10) {
-          split_pair(4);
+        } else if (ks >= 4 && ks < 8) {
+          weight(2 * (ks - 4));
+          weight(2 * (ks - 4) + 1);
+        } else if (ks >= 8 && ks < 12) {
+          split_pair(2 * (ks - 8));
         } else if (ks == 12) {
-          split_pair(6);
+          *(LDS_AS u32x4_t*)(xp_mine) = ph[kDh];
+          *(LDS_AS u32x4_t*)(xp_mine + 1024) = pl[kDh];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // values of tile i: fragment j = dim block j&7, key step j>>3. Each slot
-      // holds two MFMAs, so the second half of the softmax, the loads of tile
-      // i+2 and the publication of tile i+1's partial scores go here.
+      // every wave's weights are published; every wave has read its partner's
+      // partial scores of tile i, so the exchange area can take tile i+1's
+      __syncthreads();
+      ph[1 - kDh] = *(const LDS_AS u32x4_t*)(xp_part);
+      pl[1 - kDh] = *(const LDS_AS u32x4_t*)(xp_part + 1024);
+      *(LDS_AS f32x4_t*)(xs_mine) = (f32x4_t){sc[kSend], sc[kSend + 1], sc[kSend + 2], sc[kSend + 3]};
+      *(LDS_AS f32x4_t*)(xs_mine + 1024) =
+          (f32x4_t){sc[kSend + 4], sc[kSend + 5], sc[kSend + 6], sc[kSend + 7]};
+      __builtin_amdgcn_sched_barrier(0);
+
+      // values of tile i; tile loads in the first slots (each slot holds two
+      // MFMAs, so it has issue room to spare)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int nn = 0; nn < 16; ++nn) {
+        const int j = frag(nn);
         acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], __builtin_bit_cast(bf16x8_t, ph[j >> 3]),
                                                              acc[j & 7], 0, 0, 0);
         if (kHiLo)
           acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], __builtin_bit_cast(bf16x8_t, pl[j >> 3]),
                                                                acc[j & 7], 0, 0, 0);
-        if (j + kAhead < 16) vf[j + kAhead] = vread(j + kAhead);
-        if (j < 9 && dma)
-          issue_tile_part(dma_buf, lat_rs, rope_rs, (i + 2) * kTile, wave, lane, rope_voff, j);
-        if (j < 4) {
-          weight(8 + 2 * j); weight(9 + 2 * j);
-        } else if (j < 8) {
-          split_pair(8 + 2 * (j - 4));
-        } else if (j < 12) {
-#pragma unroll
-          for (int r = 4 * (j - 8); r < 4 * (j - 7); ++r) dst[r * 64 + lane] = sc[r];
-        }
+        if (nn + kAhead < 16) vf[frag(nn + kAhead)] = vread(frag(nn + kAhead));
+        if (nn < 9 && dma)
+          issue_tile_part(dma_buf, lat_rs, rope_rs, (i + 3) * kTile, wave, lane, rope_voff, nn);
         __builtin_amdgcn_sched_barrier(0);
       }
       own = sc;
     };
 
-    // Tile i+1 landed and tile i's partial scores are published once every
-    // wave passes the barrier; ring slot (i+2)%3 is free from then on.
-    auto advance = [&]() {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of tile i+1 landed
+    // Tile i+1 landed (tile i+2 may still be in flight) and the partner
+    // scores of tile i are published once every wave passes the barrier;
+    // ring slot (i+3)%4 is free from then on.
+    auto advance = [&](int i) {
+      if (i + 2 < ntiles)
+        __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): at most tile i+2's loads outstanding
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
     };
-    // Tiles wholly inside the prefix and the chunk need no mask; the rest
-    // (tree keys, chunk tail) take the masked step in a loop of their own, so
-    // that each loop body has a single register assignment.
-    // The unmasked loop is unrolled by the ring period so that every step's
-    // slots are compile-time objects; the remaining tiles (fewer than three
-    // unmasked ones, then the masked ones) take the masked step with the
-    // slots chosen at run time.
+    // Tiles wholly inside the prefix and the chunk need no mask. Their loop
+    // is unrolled by the ring period so that every step's slots are
+    // compile-time objects; the remaining tiles take the masked step with the
+    // slots chosen at run time (for those the compiler cannot rule out that
+    // the tile being loaded is read, so it waits for the load). Separate
+    // loops keep a single register assignment per loop body.
     const int64_t full_end = prefix < c1 ? prefix : c1;
     const int n_full = full_end > c0 ? (int)((full_end - c0) / kTile) : 0;
     int i = 0;
-    for (; i + 3 <= n_full; i += 3) {
-      advance();
-      step(std::false_type{}, r1, r0, r2, i, 0u);
-      advance();
+    for (; i + 4 <= n_full; i += 4) {
+      advance(i);
+      step(std::false_type{}, r1, r0, r3, i, 0u);
+      advance(i + 1);
       step(std::false_type{}, r2, r1, r0, i + 1, 0u);
-      advance();
-      step(std::false_type{}, r0, r2, r1, i + 2, 0u);
+      advance(i + 2);
+      step(std::false_type{}, r3, r2, r1, i + 2, 0u);
+      advance(i + 3);
+      step(std::false_type{}, r0, r3, r2, i + 3, 0u);
     }
     for (; i < ntiles; ++i) {
-      advance();
-      step(std::true_type{}, ring((i + 1) % kRing), ring(i % kRing), ring((i + 2) % kRing), i,
-           tile_visibility(c0 + (int64_t)i * kTile, c1, prefix, anc));
+      advance(i);
+      const uint32_t vis = tile_visibility(c0 + (int64_t)i * kTile, c1, prefix, anc);
+      step(std::true_type{}, ring((i + 1) & 3), ring(i & 3), ring((i + 3) & 3), i, vis);
     }
-    if (!__syncthreads_or(ovf)) break;
+    // workgroup-wide OR of the overflow flags, through the exchange area
+    // (every wave is past its last read of it once all pass the barrier)
+    __syncthreads();
+    const int wave_ovf = __builtin_amdgcn_ballot_w64(ovf != 0) != 0;  // OR over this wave's heads
+    if (lane == 0) *(LDS_AS int*)(xs + wave * 2048) = wave_ovf;
+    __syncthreads();
+    const int any_ovf = *(const LDS_AS int*)(xs) | *(const LDS_AS int*)(xs + 2048) |
+                        *(const LDS_AS int*)(xs + 4096) | *(const LDS_AS int*)(xs + 6144);
+    __syncthreads();
+    if (!any_ovf) break;
+    // redo with m_ref = the chunk's max over both waves' keys
+    *(LDS_AS float*)(xs + wave * 2048 + lane * 4) = m_seen;
+    __syncthreads();
+    m_ref = fmax3(m_seen, *(const LDS_AS float*)(xs + partner * 2048 + lane * 4));
+    have_ref = true;
     __syncthreads();
   }
 
-  // Normalise, then store through LDS (free now: no tile load is in flight
-  // after the last step) so that each global store instruction writes 1 KB of
-  // one head's row instead of 32-byte pieces of 32 rows. Staging layout: head
-  // h's row in LDS object h / 18 (ring slots 0..2, then the exchange buffer)
-  // at (h % 18) * 2048, its 128 16-byte chunks at 16 * (c ^ (h & 7)),
-  // conflict-free for both the column-wise writes and the row-wise reads.
+  // denominator: this lane pair's own keys, plus the partner wave's keys
+  // (no tile load is in flight and every wave is past its last LDS read)
+  float l_tot = partner_sum(l_run);
+  *(LDS_AS float*)(xs + wave * 2048 + lane * 4) = l_tot;
+  __syncthreads();
+  l_tot += *(const LDS_AS float*)(xs + partner * 2048 + lane * 4);
+
+  // Normalise, then store through LDS so that each global store instruction
+  // writes 1 KB of one head's row instead of 32-byte pieces of 32 rows.
+  // Staging layout: head h's row in ring slot h / 18 at (h % 18) * 2048, its
+  // 128 16-byte chunks at 16 * (c ^ (h & 7)), conflict-free for both the
+  // column-wise writes and the row-wise reads.
   auto stage_row = [&](int h) {
     const int o = h / kStageHeads;
-    LDS_AS char* base = o == 0 ? r0 : (o == 1 ? r1 : (o == 2 ? r2 : (LDS_AS char*)xs));
-    return base + (h - o * kStageHeads) * (kDl * 4);
+    return ring(o) + (h - o * kStageHeads) * (kDl * 4);
   };
-  const float l_tot = partner_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_val = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   const bool final_write = nsplit_b == 1;
@@ -603,11 +693,15 @@ void split_mfma_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char ring0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char ring1[kTileBytes];
   __shared__ __attribute__((aligned(16))) char ring2[kTileBytes];
-  __shared__ __attribute__((aligned(16))) float xs[kXsBytes / 4];
+  __shared__ __attribute__((aligned(16))) char ring3[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char xs_raw[kXchgBytes];
+  __shared__ __attribute__((aligned(16))) char xp_raw[kXchgBytes];
   LDS_AS char* r0 = (LDS_AS char*)ring0;
   LDS_AS char* r1 = (LDS_AS char*)ring1;
   LDS_AS char* r2 = (LDS_AS char*)ring2;
-  LDS_AS float* x = (LDS_AS float*)xs;
+  LDS_AS char* r3 = (LDS_AS char*)ring3;
+  LDS_AS char* xs = (LDS_AS char*)xs_raw;
+  LDS_AS char* xp = (LDS_AS char*)xp_raw;
   int b, s, t;
   if (!decode_work(a, b, s, t)) return;
   const int tid = threadIdx.x;
@@ -623,9 +717,9 @@ void split_mfma_kernel(Args a) {
   if ((int64_t)s * a.chunk >= n) return;  // this sequence needs fewer splits
   const int hh = wave >> 1;
   if ((wave & 1) == 0)
-    split_body<0, kHiLo>(a, r0, r1, r2, x, b, s, t, wave, hh, lane, row0, n);
+    split_body<0, kHiLo>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
   else
-    split_body<1, kHiLo>(a, r0, r1, r2, x, b, s, t, wave, hh, lane, row0, n);
+    split_body<1, kHiLo>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
 }
 
 // ---------------------------------------------------------------------------
