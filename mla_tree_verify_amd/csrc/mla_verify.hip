@@ -65,9 +65,9 @@ constexpr int kTileBytes = kLatBytes + kRopeBytes;  // 36864
 constexpr int kRing = 4;                         // tile slots: values, scores, two loading
 constexpr int kXchgBytes = 4 * 2 * 64 * 16;      // one exchange area: [4 waves][2 chunks][64 lanes][16 B]
 constexpr int kLdsBytes = kRing * kTileBytes + 2 * kXchgBytes;  // 163840 = all of a CU's LDS
-constexpr int kStageHeads = kTileBytes / (kDl * 4);  // 18 output rows staged per ring slot
 constexpr int kThreads = 256;
-static_assert(kRing * kStageHeads >= kHeads, "the epilogue stages a token's 64 x 512 fp32 outputs in the ring");
+static_assert(kRing * 128 == kDl && 128 * 4 * kHeads <= kTileBytes,
+              "the epilogue stages 128 output dims of all 64 heads in each ring slot");
 static_assert(kLdsBytes <= 163840, "LDS per workgroup");
 constexpr int kXcds = 8;
 constexpr int64_t kChunkGran = kTile;
@@ -130,6 +130,18 @@ __device__ inline uint64_t ancestor_mask(const int32_t* parent, int q, int t) {
   for (int step = 0; step < q && node >= 0 && node < q; ++step) {
     anc |= 1ull << node;
     node = parent[node];
+  }
+  return anc;
+}
+
+// The same mask from a wave-held copy of the tree: lane u holds parent[u]
+// (u < q). t is wave-uniform, so every step is a scalar read of one lane.
+__device__ inline uint64_t ancestor_mask_wave(int par_lane, int q, int t) {
+  uint64_t anc = 0;
+  int node = t;
+  for (int step = 0; step < q && node >= 0 && node < q; ++step) {
+    anc |= 1ull << node;
+    node = __builtin_amdgcn_readlane(par_lane, node);
   }
   return anc;
 }
@@ -229,18 +241,27 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // Latent row k lands at buf + 1024 k with its 16-byte chunks XOR-swizzled by
 // swz(k); the rope rows follow the 32 latent rows, 128 B each, swizzled by
 // swz_rope(k).
+// key_rel = kNoTile requests nothing: the byte offset is then set past any
+// descriptor range (at most 4e6 rows x 1 KB, below 2^32), so the load fills
+// the slot with zeros without reading memory (callers use it to keep the
+// number of loads per step constant).
+constexpr int kNoTile = -1;
+constexpr uint32_t kOutOfRange = 0xFFFFF000u;
 __device__ inline void issue_tile_part(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_rs,
                                        __amdgpu_buffer_rsrc_t rope_rs, int key_rel, int wave, int lane,
                                        int rope_voff, int part) {
   // The whole byte offset goes in the VGPR operand: raw-buffer range checks
   // cover the VGPR offset (plus the immediate) but not the SGPR offset.
+  const bool none = key_rel < 0;
   if (part < 8) {
     const int k = 4 * part + wave;
+    const uint32_t off = (uint32_t)(key_rel + k) * 1024u + 16u * (uint32_t)(lane ^ swz(k));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rs, (LDS_AS void*)(buf + k * 1024), 16,
-                                             (key_rel + k) * 1024 + 16 * (lane ^ swz(k)), 0, 0, 0);
+                                             (int)(none ? kOutOfRange : off), 0, 0, 0);
   } else {
+    const uint32_t off = (uint32_t)(key_rel + 8 * wave) * 128u + (uint32_t)rope_voff;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rs, (LDS_AS void*)(buf + kLatBytes + wave * 1024), 16,
-                                             (key_rel + 8 * wave) * 128 + rope_voff, 0, 0, 0);
+                                             (int)(none ? kOutOfRange : off), 0, 0, 0);
   }
 }
 
@@ -286,6 +307,19 @@ __device__ inline int k_frag_off(const KBases& kb, int ks) {
 
 __device__ inline bf16x8_t lds_b128(const LDS_AS char* p) { return *(const LDS_AS bf16x8_t*)p; }
 
+// Workgroup barrier for LDS exchanges: this wave's LDS reads and writes are
+// complete (lgkmcnt(0)) and every wave has arrived. Unlike __syncthreads(),
+// it does not wait for outstanding tile loads (that workgroup-scope fence
+// waits vmcnt(0), which would serialise the loads three steps ahead); tile
+// loads are waited for explicitly with vmcnt. The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Returns x unchanged but opaque to the optimiser, so that an address formed
 // once per loop iteration is not split into one hoisted register per use.
 __device__ inline int opaque(int x) {
@@ -327,12 +361,37 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   constexpr int kOwn = 8 * kDh;         // this wave's softmax elements
   constexpr int kSend = 8 * (1 - kDh);  // the partner's
   const int half = lane >> 5;
-  const int64_t prefix = n - a.q;
-  const int64_t c0 = (int64_t)s * a.chunk;
-  const int64_t c1 = c0 + a.chunk < n ? c0 + a.chunk : n;
-  const int nsplit_b = (int)((n + a.chunk - 1) / a.chunk);
-  const uint64_t anc = ancestor_mask(a.parent + (int64_t)b * a.q, a.q, t);
+  // sequence positions fit in 32 bits (a sequence has at most MLAV_MAX_KV rows)
+  const int n32 = (int)n;
+  const int chunk = (int)a.chunk;
+  const int prefix = n32 - a.q;
+  const int c0 = s * chunk;
+  const int c1 = c0 + chunk < n32 ? c0 + chunk : n32;
+  const int nsplit_b = (n32 + chunk - 1) / chunk;
+  const int ntiles = (c1 - c0 + kTile - 1) / kTile;
   const int head = 32 * hh + (lane & 31);
+
+  // Tile 0 is requested before anything else, then the queries and the
+  // tree, then tiles 1 and 2, so that load latency overlaps the ancestor
+  // walk and the wait before the first scores covers tile 0 and the queries
+  // only (loads complete in issue order).
+  const __amdgpu_buffer_rsrc_t lat_rs =
+      make_rsrc(a.lat + (row0 + c0) * kDl, (uint32_t)(n32 - c0) * (kDl * 2));
+  const __amdgpu_buffer_rsrc_t rope_rs =
+      make_rsrc(a.rope + (row0 + c0) * kDr, (uint32_t)(n32 - c0) * (kDr * 2));
+  // rope row 8 wave + (lane>>3) of a tile: LDS position lane&7 holds
+  // logical chunk (lane&7) ^ swz_rope(row)
+  const int rope_voff = (lane >> 3) * 128 + 16 * ((lane & 7) ^ swz_rope(8 * wave + (lane >> 3)));
+  // every step issues nine loads (tiles past the chunk end request nothing)
+  // so that vmcnt(9) always means "all but the latest tile landed"
+  auto tile_rel = [&](int i) { return i < ntiles ? i * kTile : kNoTile; };
+  auto issue_next_tiles = [&]() {
+    issue_tile(r1, lat_rs, rope_rs, tile_rel(1), wave, lane, rope_voff);
+    issue_tile(r2, lat_rs, rope_rs, tile_rel(2), wave, lane, rope_voff);
+  };
+  issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+
+  const int par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
 
   // resident queries for this wave's dim half: B operand of S^T = K Q^T
   bf16x8_t qreg[18];
@@ -362,14 +421,8 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     for (int m = 0; m < 4; ++m) vb[m] = kk * 1024 + 16 * (z0 ^ (4 * m)) + 8 * (i & 1);
   }
 
-  const int ntiles = (int)((c1 - c0 + kTile - 1) / kTile);
-  const __amdgpu_buffer_rsrc_t lat_rs =
-      make_rsrc(a.lat + (row0 + c0) * kDl, (uint32_t)((n - c0) * kDl * 2));
-  const __amdgpu_buffer_rsrc_t rope_rs =
-      make_rsrc(a.rope + (row0 + c0) * kDr, (uint32_t)((n - c0) * kDr * 2));
-  // rope row 8 wave + (lane>>3) of a tile: LDS position lane&7 holds
-  // logical chunk (lane&7) ^ swz_rope(row)
-  const int rope_voff = (lane >> 3) * 128 + 16 * ((lane & 7) ^ swz_rope(8 * wave + (lane >> 3)));
+  issue_next_tiles();
+  const uint64_t anc = ancestor_mask_wave(par_lane, a.q, t);
 
   const int partner = wave ^ 1;  // same head half, other dim half
   const KBases kb = make_kbases(lane & 31, half);
@@ -406,22 +459,21 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // prologue: tiles 0..2 in flight; tile 0's partial scores exchanged in
     // full (through ring slot 3, free until tile 3 is loaded) to fix m_ref,
     // then its partner half published for step 0
-    issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
-    if (ntiles > 1) issue_tile(r1, lat_rs, rope_rs, kTile, wave, lane, rope_voff);
-    if (ntiles > 2) issue_tile(r2, lat_rs, rope_rs, 2 * kTile, wave, lane, rope_voff);
-    if (ntiles > 2)
-      __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18): tile 0 landed
-    else if (ntiles > 1)
-      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (attempt == 1) {
+      issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+      issue_next_tiles();
+    }
+    __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18): tile 0 landed (tiles 1, 2 may be in flight)
     __syncthreads();
-    f32x16_t own = tile_scores<kDh>(r0, qreg, kb);
+    const f32x16_t s0 = tile_scores<kDh>(r0, qreg, kb);
+    float own[8];  // this wave's elements of the next tile's partial scores
+#pragma unroll
+    for (int k = 0; k < 8; ++k) own[k] = s0[kOwn + k];
     if (attempt == 0) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         *(LDS_AS f32x4_t*)(r3 + wave * 4096 + c * 1024 + lane * 16) =
-            (f32x4_t){own[4 * c], own[4 * c + 1], own[4 * c + 2], own[4 * c + 3]};
+            (f32x4_t){s0[4 * c], s0[4 * c + 1], s0[4 * c + 2], s0[4 * c + 3]};
       __syncthreads();
       const uint32_t vis0 = tile_visibility(c0, c1, prefix, anc);
       float mx = -INFINITY;
@@ -430,14 +482,14 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
         const f32x4_t p4 = *(const LDS_AS f32x4_t*)(r3 + partner * 4096 + c * 1024 + lane * 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (key_visible_bit(vis0, 4 * c + e)) mx = fmax3(mx, own[4 * c + e] + p4[e]);
+          if (key_visible_bit(vis0, 4 * c + e)) mx = fmax3(mx, s0[4 * c + e] + p4[e]);
       }
       have_ref = vis0 != 0;
       m_ref = have_ref ? partner_max(mx) * sl2 : -INFINITY;
     }
-    *(LDS_AS f32x4_t*)(xs_mine) = (f32x4_t){own[kSend], own[kSend + 1], own[kSend + 2], own[kSend + 3]};
+    *(LDS_AS f32x4_t*)(xs_mine) = (f32x4_t){s0[kSend], s0[kSend + 1], s0[kSend + 2], s0[kSend + 3]};
     *(LDS_AS f32x4_t*)(xs_mine + 1024) =
-        (f32x4_t){own[kSend + 4], own[kSend + 5], own[kSend + 6], own[kSend + 7]};
+        (f32x4_t){s0[kSend + 4], s0[kSend + 5], s0[kSend + 6], s0[kSend + 7]};
 
     // One step: softmax (own keys) and values (all keys) of tile i, scores
     // of tile i+1 (computed even past the last tile, on whatever that ring
@@ -454,7 +506,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
                     uint32_t vis) {
       constexpr bool kMasked = decltype(masked_tag)::value;
       constexpr int kAhead = 8;
-      const bool dma = i + 3 < ntiles;
+      const int dma_rel = tile_rel(i + 3);
       auto kread = [&](int ks) {
         const int cc = 36 * kDh + 2 * ks;  // even chunk of the 576-d row
         return lds_b128(kbuf + k_frag_off<kDh>(kb, ks));
@@ -516,10 +568,10 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
           vf[frag(ks + kAhead - 18)] = vread(frag(ks + kAhead - 18));
         if (ks == 0) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) sv[k] = own[kOwn + k] + pa[k];
+          for (int k = 0; k < 4; ++k) sv[k] = own[k] + pa[k];
         } else if (ks == 1) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) sv[4 + k] = own[kOwn + 4 + k] + pb[k];
+          for (int k = 0; k < 4; ++k) sv[4 + k] = own[4 + k] + pb[k];
         } else if (ks == 2) {
           if (kMasked) {
 #pragma unroll
@@ -557,7 +609,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
 
       // every wave's weights are published; every wave has read its partner's
       // partial scores of tile i, so the exchange area can take tile i+1's
-      __syncthreads();
+      lds_barrier();
       ph[1 - kDh] = *(const LDS_AS u32x4_t*)(xp_part);
       pl[1 - kDh] = *(const LDS_AS u32x4_t*)(xp_part + 1024);
       *(LDS_AS f32x4_t*)(xs_mine) = (f32x4_t){sc[kSend], sc[kSend + 1], sc[kSend + 2], sc[kSend + 3]};
@@ -576,22 +628,19 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
           acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], __builtin_bit_cast(bf16x8_t, pl[j >> 3]),
                                                                acc[j & 7], 0, 0, 0);
         if (nn + kAhead < 16) vf[frag(nn + kAhead)] = vread(frag(nn + kAhead));
-        if (nn < 9 && dma)
-          issue_tile_part(dma_buf, lat_rs, rope_rs, (i + 3) * kTile, wave, lane, rope_voff, nn);
+        if (nn < 9) issue_tile_part(dma_buf, lat_rs, rope_rs, dma_rel, wave, lane, rope_voff, nn);
         __builtin_amdgcn_sched_barrier(0);
       }
-      own = sc;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) own[k] = sc[kOwn + k];
     };
 
     // Tile i+1 landed (tile i+2 may still be in flight) and the partner
     // scores of tile i are published once every wave passes the barrier;
     // ring slot (i+3)%4 is free from then on.
-    auto advance = [&](int i) {
-      if (i + 2 < ntiles)
-        __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): at most tile i+2's loads outstanding
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __syncthreads();
+    auto advance = [&](int) {
+      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): only tile i+2's loads may be outstanding
+      lds_barrier();
     };
     // Tiles wholly inside the prefix and the chunk need no mask. Their loop
     // is unrolled by the ring period so that every step's slots are
@@ -642,42 +691,42 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   __syncthreads();
   l_tot += *(const LDS_AS float*)(xs + partner * 2048 + lane * 4);
 
-  // Normalise, then store through LDS so that each global store instruction
-  // writes 1 KB of one head's row instead of 32-byte pieces of 32 rows.
-  // Staging layout: head h's row in ring slot h / 18 at (h % 18) * 2048, its
-  // 128 16-byte chunks at 16 * (c ^ (h & 7)), conflict-free for both the
-  // column-wise writes and the row-wise reads.
-  auto stage_row = [&](int h) {
-    const int o = h / kStageHeads;
-    return ring(o) + (h - o * kStageHeads) * (kDl * 4);
-  };
+  // Stage the accumulators through LDS so that each global store writes two
+  // 512-byte row pieces instead of 32-byte pieces of 32 rows. Ring slot o
+  // takes dims [128 o, 128 o + 128) of all 64 heads (the slot of a write is
+  // then a compile-time choice); head h's 32 16-byte chunks sit at
+  // h * 512 + 16 * (c ^ (h & 15)), conflict-free for the head-per-lane writes
+  // and the chunk-per-lane reads. The reads apply 1 / l, kept per head in
+  // the weight-exchange area.
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_val = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   const bool final_write = nsplit_b == 1;
-  {
-    const int h = head;
+  if (kDh == 0 && half == 0) *(LDS_AS float*)(xp + head * 4) = inv;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+  for (int db = 0; db < 8; ++db) {
+    LDS_AS char* slot = ring(2 * kDh + (db >> 2));
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4_t v;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = acc[db][4 * g + c] * inv;
-        const int chunk = 64 * kDh + 8 * db + 2 * g + half;  // dims 4 chunk .. 4 chunk + 3
-        *(LDS_AS f32x4_t*)(stage_row(h) + 16 * (chunk ^ (h & 7))) = v;
-      }
+    for (int g = 0; g < 4; ++g) {
+      const int c = 8 * (db & 3) + 2 * g + half;
+      *(LDS_AS f32x4_t*)(slot + head * 512 + 16 * (c ^ (head & 15))) =
+          (f32x4_t){acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
     }
   }
   __syncthreads();
   const int64_t row_t = (int64_t)b * a.q + t;
   float* obase = final_write ? a.out + row_t * kHeads * kDl
                              : a.part_o + (((int64_t)b * a.nsplit + s) * a.q + t) * kHeads * kDl;
+  {
+    // this wave stores ring slot `wave`: dims [128 wave, 128 wave + 128)
+    LDS_AS char* slot = ring(wave);
+    const int c = lane & 31;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int h = 16 * wave + (k >> 1);
-    const int chunk = 64 * (k & 1) + lane;
-    const f32x4_t v = *(const LDS_AS f32x4_t*)(stage_row(h) + 16 * (chunk ^ (h & 7)));
-    *(f32x4_t*)(obase + (int64_t)h * kDl + 4 * chunk) = v;
+    for (int k = 0; k < 32; ++k) {
+      const int h = 2 * k + half;
+      const f32x4_t v = *(const LDS_AS f32x4_t*)(slot + h * 512 + 16 * (c ^ (h & 15)));
+      const float sc_h = *(const LDS_AS float*)(xp + h * 4);
+      *(f32x4_t*)(obase + (int64_t)h * kDl + 128 * wave + 4 * c) = v * sc_h;
+    }
   }
   if (kDh == 0 && half == 0) {
     if (final_write)
@@ -818,13 +867,27 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   f32x4_t accv = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
-    // unrolled so that several partial loads are in flight per thread
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) {
-      const float w = __builtin_amdgcn_exp2f((pl[s * rows_b] - M) * kLog2e);
-      wsum += w;
-      const f32x4_t o = __builtin_nontemporal_load((const f32x4_t*)(po + s * rows_b * kDl));
-      accv += w * o;
+    // Partials are loaded in batches of 16 before any is used, so that each
+    // thread keeps 16 loads in flight (the kernel is bound by memory latency
+    // times loads in flight); they are still added in split order.
+    // Entries past the last split reload the last one and get weight 0
+    // (partials are finite), so the loads need no branches.
+    constexpr int kBatch = 16;
+    for (int s0 = 0; s0 < ns; s0 += kBatch) {
+      f32x4_t o[kBatch];
+      float lz[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int sk = s0 + k < ns ? s0 + k : ns - 1;
+        o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_b * kDl));
+        lz[k] = pl[(int64_t)sk * rows_b];
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float w = s0 + k < ns ? __builtin_amdgcn_exp2f((lz[k] - M) * kLog2e) : 0.f;
+        wsum += w;
+        accv += w * o[k];
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
