@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-ms", type=float, default=400.0,
+                    help="keep warming up (untimed) until this much GPU time has passed, so clocks settle")
     ap.add_argument("--workload", default="q9_p16384")
     ap.add_argument("--rotate-mb", type=float, default=768.0, help="bytes of rotating input copies (cold run)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target host time of the oracle baseline")
@@ -133,10 +135,19 @@ def main() -> int:
         api.mla_verify(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], p, case.scale,
                        out=d["out"], lse=d["lse"], workspace=d["ws"], pv_mode=args.pv_mode)
 
-    def timed(rotate: bool) -> float:
-        for i in range(args.warmup):
-            call(copies[i % ncopy] if rotate else copies[0])
+    def warm(fn, rotate: bool = True) -> None:
+        # W untimed steps, then more until warmup_ms of wall time has passed
+        t0 = time.perf_counter()
+        i = 0
+        while i < args.warmup or (time.perf_counter() - t0) * 1e3 < args.warmup_ms:
+            fn(copies[i % ncopy] if rotate else copies[0])
+            i += 1
+            if i % 50 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
+
+    def timed(rotate: bool) -> float:
+        warm(call, rotate)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -159,9 +170,7 @@ def main() -> int:
         api.combine(d["po"], d["pl"], out=d["out"].view(-1, 512), lse=d["lse"].view(-1))
 
     def batch_us(fn) -> float:
-        for i in range(args.warmup):
-            fn(copies[i % ncopy])
-        torch.cuda.synchronize()
+        warm(fn)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)

@@ -861,33 +861,38 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   }
   const float* pl = a.part_lse + (int64_t)b * a.nsplit * rows_b + rb;
   const float* po = a.part_o + ((int64_t)b * a.nsplit * rows_b + rb) * kDl + 4 * d4;
+  // Batches of up to 32 splits: every lse and partial load of a batch is
+  // issued before any is used (one memory round trip per batch); batches are
+  // merged with a running max. Entries past the last split reload the last
+  // one and get weight 0 (partials are finite), so the loads need no branches;
+  // splits are still added in order.
+  constexpr int kBatch = 32;
   float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < ns; ++s) M = fmax3(M, pl[s * rows_b]);
   f32x4_t accv = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  if (M != -INFINITY) {
-    // Partials are loaded in batches of 16 before any is used, so that each
-    // thread keeps 16 loads in flight (the kernel is bound by memory latency
-    // times loads in flight); they are still added in split order.
-    // Entries past the last split reload the last one and get weight 0
-    // (partials are finite), so the loads need no branches.
-    constexpr int kBatch = 16;
-    for (int s0 = 0; s0 < ns; s0 += kBatch) {
-      f32x4_t o[kBatch];
-      float lz[kBatch];
+  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+    f32x4_t o[kBatch];
+    float lz[kBatch];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const int sk = s0 + k < ns ? s0 + k : ns - 1;
-        o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_b * kDl));
-        lz[k] = pl[(int64_t)sk * rows_b];
-      }
+    for (int k = 0; k < kBatch; ++k) {
+      const int sk = s0 + k < ns ? s0 + k : ns - 1;
+      lz[k] = pl[(int64_t)sk * rows_b];
+      o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_b * kDl));
+    }
+    float mb = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const float w = s0 + k < ns ? __builtin_amdgcn_exp2f((lz[k] - M) * kLog2e) : 0.f;
-        wsum += w;
-        accv += w * o[k];
-      }
+    for (int k = 0; k < kBatch; ++k) mb = fmax3(mb, lz[k]);  // reloaded entries repeat a real one
+    if (mb == -INFINITY) continue;  // every split of this batch is empty
+    const float m_new = fmax3(M, mb);
+    const float r = __builtin_amdgcn_exp2f((M - m_new) * kLog2e);  // 0 while M = -inf
+    accv *= r;
+    wsum *= r;
+    M = m_new;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = s0 + k < ns ? __builtin_amdgcn_exp2f((lz[k] - M) * kLog2e) : 0.f;
+      wsum += w;
+      accv += w * o[k];
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
