@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
                     help="after timing, run one device copy of this size (counter calibration)")
     ap.add_argument("--pv-mode", type=int, default=0)
+    ap.add_argument("--partials", type=int, default=0, help="0: int16 split partials (default), 1: fp32")
     return ap.parse_args()
 
 
@@ -94,6 +95,8 @@ def main() -> int:
                           "n_gpus": args.gpus}))
         return 2
 
+    import ctypes
+
     import numpy as np
     import torch
 
@@ -115,6 +118,8 @@ def main() -> int:
     flops = orc.algorithmic_flops(case.tree_parent, p)
     alg_bytes = orc.algorithmic_bytes(q, n)
     plan = api.device_plan(q, 1, n, n, pv_mode=args.pv_mode)
+    lib = _lib.load()
+    ws_bytes = _lib.workspace_size(q, 64, 1, n, n, pv_mode=args.pv_mode, partials=args.partials)
 
     host = {k: getattr(case, k) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
     per_copy = sum(t.numel() * t.element_size() for t in host.values()) + q * 64 * 513 * 4 * (plan.nsplit + 1)
@@ -124,16 +129,26 @@ def main() -> int:
         d = {k: v.to(dev) for k, v in host.items()}
         d["out"] = torch.empty(q, 64, 512, dtype=torch.float32, device=dev)
         d["lse"] = torch.empty(q, 64, dtype=torch.float32, device=dev)
-        ws = _lib.workspace_size(q, 64, 1, n, n, pv_mode=args.pv_mode)
-        d["ws"] = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
-        d["po"] = torch.empty(plan.nsplit, q, 64, 512, dtype=torch.float32, device=dev)
-        d["pl"] = torch.empty(plan.nsplit, q, 64, dtype=torch.float32, device=dev)
+        d["ws"] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         copies.append(d)
     stream = torch.cuda.current_stream(dev)
+    # Each timed call goes straight to the C ABI with prebuilt arguments, so
+    # that host-side argument handling does not gap the back-to-back launches.
+    # phase 0 = the whole call, 1 = the split kernel alone, 2 = the combine
+    # kernel alone (on the workspace phase 1 filled).
+    opts = [_lib.options(0, args.pv_mode, 0, args.partials, ph) for ph in range(3)]
+    for d in copies:
+        d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
+                      d["k_rope"].data_ptr(), d["tree_parent"].data_ptr(), p, ctypes.c_float(case.scale),
+                      d["out"].data_ptr(), d["lse"].data_ptr(), q, 64, d["ws"].data_ptr(), ws_bytes,
+                      stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
+    for ph in range(3):
+        rc = lib.mla_verify_ex(*copies[0]["args"][ph])
+        if rc != _lib.MLAV_OK:
+            raise _lib.MLAVError(rc, f"mla_verify_ex (phase {ph})")
 
     def call(d):
-        api.mla_verify(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], p, case.scale,
-                       out=d["out"], lse=d["lse"], workspace=d["ws"], pv_mode=args.pv_mode)
+        lib.mla_verify_ex(*d["args"][0])
 
     def warm(fn, rotate: bool = True) -> None:
         # W untimed steps, then more until warmup_ms of wall time has passed
@@ -163,11 +178,10 @@ def main() -> int:
     # each kernel alone: K back-to-back launches (rotating inputs) between two
     # events recorded on the stream the library launches on
     def split(d):
-        api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], p,
-                                case.scale, plan, part_out=d["po"], part_lse=d["pl"], pv_mode=args.pv_mode)
+        lib.mla_verify_ex(*d["args"][1])
 
     def merge(d):
-        api.combine(d["po"], d["pl"], out=d["out"].view(-1, 512), lse=d["lse"].view(-1))
+        lib.mla_verify_ex(*d["args"][2])
 
     def batch_us(fn) -> float:
         warm(fn)
@@ -239,7 +253,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": n, "heads": 64, "dl": 512,
                    "dr": 64, "tree": case.meta["tree"], "scale": case.scale, "nsplit": plan.nsplit,
-                   "chunk": plan.chunk, "pv_mode": args.pv_mode, "parallelism": "single GPU"},
+                   "chunk": plan.chunk, "pv_mode": args.pv_mode, "partials": "int16" if args.partials == 0 else "fp32",
+                   "parallelism": "single GPU"},
         "us_per_call": round(us_cold, 2),
         "us_per_call_warm": round(us_warm, 2),
         "tflops_warm": round(tflops_warm, 2),

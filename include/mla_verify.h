@@ -81,7 +81,18 @@ typedef struct mlav_options {
                       1: a single bf16 weight (8 bits; faster, looser) */
   int32_t kernel;  /* 0: bf16 MFMA kernel (default); 1: plain fp32 VALU kernel
                       (a slow second implementation kept for cross-checks) */
-  int32_t reserved; /* must be 0 */
+  int32_t partials; /* storage of the split partials between the two kernels of
+                       mla_verify / _ex / _batched:
+                       0: int16 values with one fp32 scale per (row, split)
+                          (the default; each value is off by at most 2^-16 of
+                          the largest |value| of its row, and the partial
+                          traffic is half that of fp32);
+                       1: fp32 values (the format mla_verify_partials writes) */
+  int32_t phase;    /* 0: the whole call; 1: the split kernel only (with more than
+                       one split the partials stay in the workspace); 2: the
+                       combine kernel only, on the workspace that a phase-1 call
+                       with the same arguments filled (nothing runs when the plan
+                       has one split: phase 1 then wrote out and lse) */
 } mlav_options;
 
 /* What the planner decided for one call. */
@@ -137,7 +148,8 @@ int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, cons
                            int32_t num_heads, void* workspace, size_t workspace_bytes,
                            void* stream, const mlav_options* opt);
 
-/* Workspace bytes a call with these sizes needs (0 when no split is needed).
+/* Workspace bytes a call with these sizes and options needs (0 when no split
+   is needed); it depends on opt->partials.
    num_cus = 0 queries the current HIP device; pass the CU count to plan
    without a device. For one sequence use batch = 1 and
    total_kv = max_kv = prefix_len + q_len. Returns 0 for invalid sizes. */

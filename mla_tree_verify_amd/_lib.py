@@ -37,7 +37,8 @@ EXPORTS = (
 
 
 class Options(ctypes.Structure):
-    _fields_ = [("nsplit", c_int32), ("pv_mode", c_int32), ("kernel", c_int32), ("reserved", c_int32)]
+    _fields_ = [("nsplit", c_int32), ("pv_mode", c_int32), ("kernel", c_int32), ("partials", c_int32),
+                ("phase", c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -96,8 +97,8 @@ def strerror(status: int) -> str:
     return load().mla_verify_strerror(status).decode()
 
 
-def options(nsplit: int = 0, pv_mode: int = 0, kernel: int = 0) -> Options:
-    return Options(nsplit, pv_mode, kernel, 0)
+def options(nsplit: int = 0, pv_mode: int = 0, kernel: int = 0, partials: int = 0, phase: int = 0) -> Options:
+    return Options(nsplit, pv_mode, kernel, partials, phase)
 
 
 def plan(q_len: int, num_heads: int, batch: int, total_kv: int, max_kv: int, num_cus: int,
@@ -112,8 +113,8 @@ def plan(q_len: int, num_heads: int, batch: int, total_kv: int, max_kv: int, num
 
 
 def workspace_size(q_len: int, num_heads: int, batch: int, total_kv: int, max_kv: int, num_cus: int = 0,
-                   nsplit: int = 0, pv_mode: int = 0, kernel: int = 0) -> int:
-    opt = options(nsplit, pv_mode, kernel)
+                   nsplit: int = 0, pv_mode: int = 0, kernel: int = 0, partials: int = 0) -> int:
+    opt = options(nsplit, pv_mode, kernel, partials)
     return int(load().mla_verify_workspace_size(q_len, num_heads, batch, total_kv, max_kv, num_cus,
                                                  ctypes.byref(opt)))
 

@@ -41,9 +41,11 @@ def mla_verify(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tens
                tree_parent: torch.Tensor, prefix_len: int, scale: float,
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None, nsplit: int = 0, pv_mode: int = 0,
-               kernel: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+               kernel: int = 0, partials: int = 0, phase: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """One sequence: q_nope [q,H,512], q_rope [q,H,64], kv_latent [P+q,512], k_rope [P+q,64]
-    (bf16), tree_parent [q] int32 -> out [q,H,512] fp32, lse [q,H] fp32."""
+    (bf16), tree_parent [q] int32 -> out [q,H,512] fp32, lse [q,H] fp32.
+    partials: 0 = int16 split partials with per-row scales (default), 1 = fp32.
+    phase: 0 = whole call, 1 = split kernel only, 2 = combine kernel only (same workspace)."""
     if not q_nope.is_cuda:
         raise ValueError("inputs must be on a GPU (the library has no CPU path)")
     dev = q_nope.device
@@ -61,7 +63,7 @@ def mla_verify(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tens
     _check(out, "out", torch.float32, (q, h, DL), dev)
     _check(lse, "lse", torch.float32, (q, h), dev)
     lib = _lib.load()
-    opt = _lib.options(nsplit, pv_mode, kernel)
+    opt = _lib.options(nsplit, pv_mode, kernel, partials, phase)
     need = int(lib.mla_verify_workspace_size(q, h, 1, n, n, 0, ctypes.byref(opt)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -80,7 +82,7 @@ def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: to
                        scale: float, max_kv: Optional[int] = None,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, nsplit: int = 0, pv_mode: int = 0,
-                       kernel: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                       kernel: int = 0, partials: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """B sequences: q_nope [B,q,H,512], kv rows of sequence b = [off[b], off[b+1]),
     tree_parent [B,q] int32, kv_offsets [B+1] int64 (CPU or device)."""
     if not q_nope.is_cuda:
@@ -106,7 +108,7 @@ def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: to
     _check(out, "out", torch.float32, (bsz, q, h, DL), dev)
     _check(lse, "lse", torch.float32, (bsz, q, h), dev)
     lib = _lib.load()
-    opt = _lib.options(nsplit, pv_mode, kernel)
+    opt = _lib.options(nsplit, pv_mode, kernel, partials)
     need = int(lib.mla_verify_workspace_size(q, h, bsz, total, max_kv, 0, ctypes.byref(opt)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

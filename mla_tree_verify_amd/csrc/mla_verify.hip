@@ -92,7 +92,9 @@ struct Args {
   const int64_t* offs;   // [B + 1] or null (one sequence of single_n rows)
   float* out;            // [B, q, H, 512]
   float* lse;            // [B, q, H]
-  float* part_o;         // [B, S, q, H, 512]
+  float* part_o;         // [B, S, q, H, 512] fp32 partials
+  int16_t* part_q;       // [B, S, q, H, 512] compact partials (int16 x part_scale)
+  float* part_scale;     // [B, S, q, H]
   float* part_lse;       // [B, S, q, H]
   int64_t single_n;
   int64_t total_kv;
@@ -196,6 +198,24 @@ __device__ inline float partner_max(float x) {
 __device__ inline float partner_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int kCtrl>
+__device__ inline float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+
+// Maximum over the 64 lanes of a wave, returned in every lane: quad_perm
+// steps within quads, mirrors within rows of 16, then the row-pair and
+// wave-half swaps.
+__device__ inline float wave_max(float x) {
+  x = fmax3(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmax3(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmax3(x, dpp_f32<0x141>(x));  // row_half_mirror
+  x = fmax3(x, dpp_f32<0x140>(x));  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmax3(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return partner_max(x);
 }
 
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -354,7 +374,7 @@ __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&
 // tile load into one slot does not write the slots being read and issues no
 // wait for it), an 8 KB partial-score exchange and an 8 KB weight exchange:
 // 163840 bytes. A tile is loaded three steps ahead of its value product.
-template <int kDh, bool kHiLo>
+template <int kDh, bool kHiLo, bool kCompact>
 __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r1, LDS_AS char* r2,
                                   LDS_AS char* r3, LDS_AS char* xs, LDS_AS char* xp, int b, int s,
                                   int t, int wave, int hh, int lane, int64_t row0, int64_t n) {
@@ -661,6 +681,23 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       advance(i + 3);
       step(std::false_type{}, r0, r3, r2, i + 3, 0u);
     }
+    // up to three more whole tiles: i is a multiple of 4 here, so their ring
+    // slots are still compile-time objects
+    if (i < n_full) {
+      advance(i);
+      step(std::false_type{}, r1, r0, r3, i, 0u);
+      ++i;
+      if (i < n_full) {
+        advance(i);
+        step(std::false_type{}, r2, r1, r0, i, 0u);
+        ++i;
+        if (i < n_full) {
+          advance(i);
+          step(std::false_type{}, r3, r2, r1, i, 0u);
+          ++i;
+        }
+      }
+    }
     for (; i < ntiles; ++i) {
       advance(i);
       const uint32_t vis = tile_visibility(c0 + (int64_t)i * kTile, c1, prefix, anc);
@@ -701,6 +738,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_val = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   const bool final_write = nsplit_b == 1;
+  const bool compact = kCompact && !final_write;
   if (kDh == 0 && half == 0) *(LDS_AS float*)(xp + head * 4) = inv;
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
@@ -714,9 +752,42 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   }
   __syncthreads();
   const int64_t row_t = (int64_t)b * a.q + t;
-  float* obase = final_write ? a.out + row_t * kHeads * kDl
-                             : a.part_o + (((int64_t)b * a.nsplit + s) * a.q + t) * kHeads * kDl;
-  {
+  const int64_t prow = (((int64_t)b * a.nsplit + s) * a.q + t) * kHeads;  // first partial row
+  if (compact) {
+    // Compact partials: row h (one head) of the normalised partial is stored
+    // as 512 int16 values q with one fp32 scale, value = q * scale, where
+    // scale = (largest |value| of the row) / 32767; rounding to nearest keeps
+    // every value within scale / 2, i.e. 2^-16 of the row's largest. Wave w
+    // handles heads [16 w, 16 w + 16) whole; lane l holds dims [8 l, 8 l + 8)
+    // (ring slot l >> 4), so the row max is one wave reduction and each row
+    // leaves as one contiguous 1 KB store.
+    LDS_AS char* slot = ring(lane >> 4);
+    const int cl = 2 * (lane & 15);
+    float my_scale = 0.f;  // lane k < 16 keeps the scale of head 16 w + k
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      const int h = 16 * wave + k;
+      const f32x4_t v0 = *(const LDS_AS f32x4_t*)(slot + h * 512 + 16 * (cl ^ k));
+      const f32x4_t v1 = *(const LDS_AS f32x4_t*)(slot + h * 512 + 16 * ((cl + 1) ^ k));
+      float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v0[0]), __builtin_fabsf(v0[1])),
+                                __builtin_fmaxf(__builtin_fabsf(v0[2]), __builtin_fabsf(v0[3])));
+      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v1[0]), __builtin_fabsf(v1[1])),
+                                             __builtin_fmaxf(__builtin_fabsf(v1[2]), __builtin_fabsf(v1[3]))));
+      m = wave_max(m);  // largest |acc| of the row (unnormalised)
+      // v / m lies in [-1, 1]; v_cvt_pknorm_i16_f32 scales by 32767, rounds
+      // to nearest and packs two values
+      const float g = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+      auto q2 = [&](float x, float y) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(x * g, y * g));
+      };
+      *(u32x4_t*)(a.part_q + (prow + h) * kDl + 8 * lane) =
+          (u32x4_t){q2(v0[0], v0[1]), q2(v0[2], v0[3]), q2(v1[0], v1[1]), q2(v1[2], v1[3])};
+      const float sc = m * *(const LDS_AS float*)(xp + h * 4) * (1.f / 32767.f);
+      my_scale = lane == k ? sc : my_scale;
+    }
+    if (lane < 16) a.part_scale[prow + 16 * wave + lane] = my_scale;
+  } else {
+    float* obase = final_write ? a.out + row_t * kHeads * kDl : a.part_o + prow * kDl;
     // this wave stores ring slot `wave`: dims [128 wave, 128 wave + 128)
     LDS_AS char* slot = ring(wave);
     const int c = lane & 31;
@@ -732,11 +803,11 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     if (final_write)
       a.lse[row_t * kHeads + head] = lse_val;
     else
-      a.part_lse[(((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head] = lse_val;
+      a.part_lse[prow + head] = lse_val;
   }
 }
 
-template <bool kHiLo>
+template <bool kHiLo, bool kCompact>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_mfma_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char ring0[kTileBytes];
@@ -766,9 +837,9 @@ void split_mfma_kernel(Args a) {
   if ((int64_t)s * a.chunk >= n) return;  // this sequence needs fewer splits
   const int hh = wave >> 1;
   if ((wave & 1) == 0)
-    split_body<0, kHiLo>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
+    split_body<0, kHiLo, kCompact>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
   else
-    split_body<1, kHiLo>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
+    split_body<1, kHiLo, kCompact>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -840,6 +911,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(Args a) {
 // ---------------------------------------------------------------------------
 // combine: log-sum-exp merge of the split partials, 128 threads per row
 // ---------------------------------------------------------------------------
+template <bool kCompact>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows) {
   const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
   if (row >= rows) return;
@@ -861,6 +933,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   }
   const float* pl = a.part_lse + (int64_t)b * a.nsplit * rows_b + rb;
   const float* po = a.part_o + ((int64_t)b * a.nsplit * rows_b + rb) * kDl + 4 * d4;
+  const float* psc = a.part_scale + (int64_t)b * a.nsplit * rows_b + rb;
+  const int16_t* pq = a.part_q + ((int64_t)b * a.nsplit * rows_b + rb) * kDl + 4 * d4;
   // Batches of up to 32 splits: every lse and partial load of a batch is
   // issued before any is used (one memory round trip per batch); batches are
   // merged with a running max. Entries past the last split reload the last
@@ -872,12 +946,22 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   float wsum = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kBatch) {
     f32x4_t o[kBatch];
-    float lz[kBatch];
+    float lz[kBatch], scl[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int sk = s0 + k < ns ? s0 + k : ns - 1;
       lz[k] = pl[(int64_t)sk * rows_b];
-      o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_b * kDl));
+      if (kCompact) {
+        // four int16 values (8 bytes), widened exactly; the scale is applied with the weight
+        typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+        const i32x2_t w2 = __builtin_nontemporal_load((const i32x2_t*)(pq + (int64_t)sk * rows_b * kDl));
+        scl[k] = psc[(int64_t)sk * rows_b];
+        o[k] = (f32x4_t){(float)((w2[0] << 16) >> 16), (float)(w2[0] >> 16), (float)((w2[1] << 16) >> 16),
+                         (float)(w2[1] >> 16)};
+      } else {
+        scl[k] = 1.f;
+        o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_b * kDl));
+      }
     }
     float mb = -INFINITY;
 #pragma unroll
@@ -892,7 +976,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
     for (int k = 0; k < kBatch; ++k) {
       const float w = s0 + k < ns ? __builtin_amdgcn_exp2f((lz[k] - M) * kLog2e) : 0.f;
       wsum += w;
-      accv += w * o[k];
+      accv += (kCompact ? w * scl[k] : w) * o[k];
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -925,7 +1009,7 @@ int device_cus(int32_t* out) {
 int check_options(const mlav_options* opt) {
   if (!opt) return MLAV_OK;
   if (opt->nsplit < 0 || opt->pv_mode < 0 || opt->pv_mode > 1 || opt->kernel < 0 ||
-      opt->kernel > 1 || opt->reserved != 0)
+      opt->kernel > 1 || opt->partials < 0 || opt->partials > 1 || opt->phase < 0 || opt->phase > 2)
     return MLAV_ERR_ARG;
   return MLAV_OK;
 }
@@ -970,9 +1054,35 @@ int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t
   return MLAV_OK;
 }
 
-size_t workspace_bytes_for(const mlav_plan& p, int32_t q, int32_t batch) {
+// Split partials in the workspace: values, then lse, then (compact only) the
+// per-row scales. Compact values are int16: [B, S, q, H, 512] x 2 bytes.
+bool compact_partials(const mlav_options* opt) {
+  // the VALU cross-check kernel writes fp32 partials only
+  return (opt ? opt->partials : 0) == 0 && (opt ? opt->kernel : 0) == 0;
+}
+
+size_t workspace_bytes_for(const mlav_plan& p, int32_t q, int32_t batch, bool compact) {
   if (!p.combine) return 0;
-  return (size_t)batch * p.nsplit * q * kHeads * (kDl + 1) * sizeof(float);
+  const size_t rows = (size_t)batch * p.nsplit * q * kHeads;
+  return compact ? rows * (kDl * sizeof(int16_t) + 2 * sizeof(float)) : rows * (kDl + 1) * sizeof(float);
+}
+
+// Points the partial pointers of `a` into the workspace (layout above).
+void set_partials(Args& a, void* workspace, const mlav_plan& p, int32_t q, int32_t batch, bool compact) {
+  const size_t rows = (size_t)batch * p.nsplit * q * kHeads;
+  a.part_o = nullptr;
+  a.part_q = nullptr;
+  a.part_scale = nullptr;
+  a.part_lse = nullptr;
+  if (!p.combine) return;
+  if (compact) {
+    a.part_q = (int16_t*)workspace;
+    a.part_lse = (float*)(a.part_q + rows * kDl);
+    a.part_scale = a.part_lse + rows;
+  } else {
+    a.part_o = (float*)workspace;
+    a.part_lse = a.part_o + rows * kDl;
+  }
 }
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
@@ -987,18 +1097,33 @@ int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* 
   a.fixed_ns = 0;
   const int kernel = opt ? opt->kernel : 0;
   const int pv_mode = opt ? opt->pv_mode : 0;
+  const bool compact = a.part_q != nullptr;
+  const int phase = opt ? opt->phase : 0;
+  if (phase == 2) goto merge;
   if (kernel == 0) {
-    if (pv_mode == 0)
-      hipLaunchKernelGGL(split_mfma_kernel<true>, dim3(p.grid), dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL(split_mfma_kernel<false>, dim3(p.grid), dim3(kThreads), 0, st, a);
+    if (pv_mode == 0) {
+      if (compact)
+        hipLaunchKernelGGL((split_mfma_kernel<true, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL((split_mfma_kernel<true, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
+    } else {
+      if (compact)
+        hipLaunchKernelGGL((split_mfma_kernel<false, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL((split_mfma_kernel<false, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
+    }
   } else {
     hipLaunchKernelGGL(split_valu_kernel, dim3(p.grid), dim3(kThreads), 0, st, a);
   }
   if (hipGetLastError() != hipSuccess) return MLAV_ERR_HIP;
+  if (phase == 1) return MLAV_OK;
+merge:
   if (p.combine) {
     const int64_t rows = (int64_t)a.batch * a.q * kHeads;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
+    if (compact)
+      hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
+    else
+      hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
     if (hipGetLastError() != hipSuccess) return MLAV_ERR_HIP;
   }
   return MLAV_OK;
@@ -1035,7 +1160,7 @@ size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch
   if (num_cus <= 0 && device_cus(&num_cus) != MLAV_OK) return 0;
   mlav_plan p;
   if (plan_impl(q_len, num_heads, batch, total_kv, max_kv, num_cus, opt, &p) != MLAV_OK) return 0;
-  return workspace_bytes_for(p, q_len, batch);
+  return workspace_bytes_for(p, q_len, batch, compact_partials(opt));
 }
 
 int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
@@ -1054,7 +1179,8 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
   mlav_plan p;
   rc = plan_impl(q_len, num_heads, 1, n, n, cus, opt, &p);
   if (rc != MLAV_OK) return rc;
-  const size_t need = workspace_bytes_for(p, q_len, 1);
+  const bool compact = compact_partials(opt);
+  const size_t need = workspace_bytes_for(p, q_len, 1, compact);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
   Args a{};
@@ -1066,8 +1192,7 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
   a.offs = nullptr;
   a.out = out;
   a.lse = lse;
-  a.part_o = (float*)workspace;
-  a.part_lse = need ? (float*)workspace + (size_t)p.nsplit * q_len * kHeads * kDl : nullptr;
+  set_partials(a, workspace, p, q_len, 1, compact);
   a.single_n = n;
   a.total_kv = n;
   a.max_kv = n;
@@ -1104,7 +1229,8 @@ int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, cons
   mlav_plan p;
   rc = plan_impl(q_len, num_heads, batch, total_kv, max_kv, cus, opt, &p);
   if (rc != MLAV_OK) return rc;
-  const size_t need = workspace_bytes_for(p, q_len, batch);
+  const bool compact = compact_partials(opt);
+  const size_t need = workspace_bytes_for(p, q_len, batch, compact);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
   Args a{};
@@ -1116,9 +1242,7 @@ int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, cons
   a.offs = kv_offsets;
   a.out = out;
   a.lse = lse;
-  a.part_o = (float*)workspace;
-  a.part_lse =
-      need ? (float*)workspace + (size_t)batch * p.nsplit * q_len * kHeads * kDl : nullptr;
+  set_partials(a, workspace, p, q_len, batch, compact);
   a.single_n = 0;
   a.total_kv = total_kv;
   a.max_kv = max_kv;
@@ -1193,7 +1317,7 @@ int32_t mla_verify_combine(const float* part_out, const float* part_lse, int32_t
   a.nsplit = nsplit;
   a.fixed_ns = nsplit;
   a.chunk = 1;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0,
                      (hipStream_t)stream, a, rows);
   return hipGetLastError() == hipSuccess ? MLAV_OK : MLAV_ERR_HIP;
 }

@@ -78,8 +78,13 @@ def test_plan_batched(lib):
 def test_workspace_size(lib):
     n = 16393
     pl = _lib.plan(9, 64, 1, n, n, 256)
+    # default: int16 partials (1024 B per row) plus an fp32 lse and an fp32 scale per row
     ws = _lib.workspace_size(9, 64, 1, n, n, num_cus=256)
-    assert ws == pl.nsplit * 9 * 64 * 513 * 4
+    assert ws == pl.nsplit * 9 * 64 * (512 * 2 + 4 + 4)
+    # fp32 partials: 512 values and an lse per row
+    assert _lib.workspace_size(9, 64, 1, n, n, num_cus=256, partials=1) == pl.nsplit * 9 * 64 * 513 * 4
+    # the VALU cross-check kernel always uses fp32 partials
+    assert _lib.workspace_size(9, 64, 1, n, n, num_cus=256, kernel=1) == pl.nsplit * 9 * 64 * 513 * 4
     assert _lib.workspace_size(9, 64, 1, 265, 265, num_cus=256, nsplit=1) == 0
     assert _lib.workspace_size(9, 32, 1, n, n, num_cus=256) == 0  # unsupported -> 0
     assert _lib.workspace_size(0, 64, 1, n, n, num_cus=256) == 0
@@ -132,9 +137,10 @@ def test_host_validation_errors(lib):
     assert call(lib, scale=float("inf")) == _lib.MLAV_ERR_ARG
     assert call(lib, scale=0.0) == _lib.MLAV_ERR_ARG
     assert call(lib, scale=-0.5) == _lib.MLAV_ERR_ARG
-    bad = _lib.Options(0, 0, 0, 1)
-    assert lib.mla_verify_ex(A, A, A, A, A, 100, 0.07, A, A, 9, 64, None, 0, None,
-                             ctypes.byref(bad)) == _lib.MLAV_ERR_ARG
+    for bad in (_lib.Options(0, 0, 0, 2, 0), _lib.Options(0, 0, 0, -1, 0), _lib.Options(0, 0, 0, 0, 3),
+                _lib.Options(0, 0, 2, 0, 0), _lib.Options(0, 2, 0, 0, 0), _lib.Options(-1, 0, 0, 0, 0)):
+        assert lib.mla_verify_ex(A, A, A, A, A, 100, 0.07, A, A, 9, 64, None, 0, None,
+                                 ctypes.byref(bad)) == _lib.MLAV_ERR_ARG
 
 
 def test_batched_validation_errors(lib):

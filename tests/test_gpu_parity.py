@@ -108,7 +108,7 @@ def test_split_count_invariance():
     ro, rl = oracle(case)
     outs = {}
     for ns in (1, 2, 3, 7, 0, 94):
-        out, lse = run(case, nsplit=ns)
+        out, lse = run(case, nsplit=ns, partials=1)  # fp32 partials: only reassociation differs
         assert_parity(out, lse, ro, rl, f"nsplit={ns}")
         outs[ns] = (out, lse)
     base_o, base_l = outs[1]
@@ -251,7 +251,7 @@ def test_workspace_too_small_is_rejected():
 def test_partials_then_combine_equals_full_call():
     case = gen.make_workload("q9_p16384")
     d = dev_case(case)
-    out, lse = run(case)
+    out, lse = run(case, partials=1)
     pl = api.device_plan(case.q_len, 1, case.prefix_len + case.q_len, case.prefix_len + case.q_len)
     po, pls = api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
                                       case.prefix_len, case.scale, pl)
@@ -276,3 +276,23 @@ def test_partials_merge_like_the_oracle_merge():
     m_o, m_l = orc.lse_merge(list(po.cpu().double().numpy()), list(pls.cpu().double().numpy()))
     assert np.abs(m_o - o_all.cpu().view(q, 64, 512).double().numpy()).max() <= 1e-5
     assert np.abs(m_l - l_all.cpu().view(q, 64).double().numpy()).max() <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["q9_p16384", "q33_p16384_peaky", "q9_p65536_chain"])
+def test_compact_partials_within_bound(name):
+    """int16 split partials (the default) against fp32 partials on the same
+    split plan. Each stored partial is within scale/2 = (largest |value| of its
+    row) / 65534 of the fp32 one; the combine takes a convex combination of the
+    partials of a row and each partial row is a convex combination of value
+    rows, so every output is within max|kv_latent| / 65534 of the fp32-partial
+    output (plus fp32 rounding). The lse does not depend on the stored values."""
+    case = gen.make_workload(name)
+    oc, lc = run(case)
+    of, lf = run(case, partials=1)
+    bound = case.kv_latent.float().abs().max().item() / 65534.0
+    diff = (oc - of).abs().max().item()
+    assert diff <= bound * 1.01 + 1e-6, f"{name}: compact vs fp32 partials differ by {diff:.3e} > {bound:.3e}"
+    assert torch.equal(lc, lf)
+    ro, rl = oracle(case) if name != "q9_p65536_chain" else (None, None)
+    if ro is not None:
+        assert_parity(oc, lc, ro, rl, f"{name} compact partials")
