@@ -54,12 +54,13 @@ def source_digest() -> str:
     return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per split-kernel launch from the committed counter summary,
-    or None when there is none or the kernel source changed since."""
+def read_counters(workload: str):
+    """HBM bytes per split-kernel launch and its MFMA-busy fraction from the
+    committed counter summary, or (None, None) when there is none or the
+    kernel source changed since."""
     path = os.path.join(PROFILES, f"split_mfma_kernel_{workload}_counters.txt")
     if not os.path.exists(path):
-        return None
+        return None, None
     kv = {}
     for line in open(path):
         line = line.strip()
@@ -67,11 +68,16 @@ def read_traffic(workload: str):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
     if kv.get("source_sha256_16") != source_digest():
-        return None
+        return None, None
     try:
-        return int(float(kv["hbm_bytes_per_launch"]))
+        traffic = int(float(kv["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
-        return None
+        traffic = None
+    try:
+        busy = float(kv["mfma_busy_fraction"])
+    except (KeyError, ValueError):
+        busy = None
+    return traffic, busy
 
 
 def blas_threads() -> int:
@@ -236,7 +242,7 @@ def main() -> int:
     tflops = flops / (us_cold * 1e-6) / 1e12
     tflops_warm = flops / (us_warm * 1e-6) / 1e12
     achieved = flops / (split_us * 1e-6) / 1e12
-    traffic = read_traffic(args.workload)
+    traffic, mfma_busy = read_counters(args.workload)
     res = {
         "metric": "MLA verify attention us/call + TFLOP/s (% MFMA peak), H=64 q_len=9, prefix 16k",
         "value": round(tflops, 2),
@@ -267,7 +273,8 @@ def main() -> int:
         "algorithmic_mb": round(alg_bytes / 1e6, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "split_mfma_kernel", "algorithmic_flop_per_launch": flops},
+                     "kernel": "split_mfma_kernel", "algorithmic_flop_per_launch": flops,
+                     "mfma_busy_counter": mfma_busy},
         "cpu_baseline": cpu,
         "parity": parity,
         "baseline_note": "vs_baseline divides by the pages' final sm_120 kernel at q9/16k (4782.6 us, fp32, RTX PRO "

@@ -218,6 +218,31 @@ __device__ inline float wave_max(float x) {
   return partner_max(x);
 }
 
+// Maximum / sum over the 16 lanes of each row of a wave, in every lane of the
+// row; the 32-lane forms add the row-pair swap (lanes 0..31 and 32..63).
+__device__ inline float row16_max(float x) {
+  x = fmax3(x, dpp_f32<0xB1>(x));
+  x = fmax3(x, dpp_f32<0x4E>(x));
+  x = fmax3(x, dpp_f32<0x141>(x));
+  return fmax3(x, dpp_f32<0x140>(x));
+}
+__device__ inline float row16_sum(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  return x + dpp_f32<0x140>(x);
+}
+__device__ inline float half32_max(float x) {
+  x = row16_max(x);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax3(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half32_sum(float x) {
+  x = row16_sum(x);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ inline int64_t uniform64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -822,6 +847,11 @@ void split_mfma_kernel(Args a) {
   LDS_AS char* r3 = (LDS_AS char*)ring3;
   LDS_AS char* xs = (LDS_AS char*)xs_raw;
   LDS_AS char* xp = (LDS_AS char*)xp_raw;
+  // Fetch the kernel arguments the prologue needs in one round of scalar
+  // loads (fetched lazily, each group would wait on its own round trip).
+  asm volatile("" ::"s"(a.qn), "s"(a.qr), "s"(a.lat), "s"(a.rope), "s"(a.parent), "s"(a.offs),
+               "s"(a.single_n), "s"(a.total_kv), "s"(a.max_kv), "s"(a.chunk), "s"(a.scale_log2), "s"(a.q),
+               "s"(a.nsplit), "s"(a.nwork), "s"(a.per_xcd));
   int b, s, t;
   if (!decode_work(a, b, s, t)) return;
   const int tid = threadIdx.x;
@@ -911,7 +941,6 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(Args a) {
 // ---------------------------------------------------------------------------
 // combine: log-sum-exp merge of the split partials, 128 threads per row
 // ---------------------------------------------------------------------------
-template <bool kCompact>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows) {
   const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
   if (row >= rows) return;
@@ -933,8 +962,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   }
   const float* pl = a.part_lse + (int64_t)b * a.nsplit * rows_b + rb;
   const float* po = a.part_o + ((int64_t)b * a.nsplit * rows_b + rb) * kDl + 4 * d4;
-  const float* psc = a.part_scale + (int64_t)b * a.nsplit * rows_b + rb;
-  const int16_t* pq = a.part_q + ((int64_t)b * a.nsplit * rows_b + rb) * kDl + 4 * d4;
   // Batches of up to 32 splits: every lse and partial load of a batch is
   // issued before any is used (one memory round trip per batch); batches are
   // merged with a running max. Entries past the last split reload the last
@@ -946,22 +973,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   float wsum = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kBatch) {
     f32x4_t o[kBatch];
-    float lz[kBatch], scl[kBatch];
+    float lz[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int sk = s0 + k < ns ? s0 + k : ns - 1;
       lz[k] = pl[(int64_t)sk * rows_b];
-      if (kCompact) {
-        // four int16 values (8 bytes), widened exactly; the scale is applied with the weight
-        typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
-        const i32x2_t w2 = __builtin_nontemporal_load((const i32x2_t*)(pq + (int64_t)sk * rows_b * kDl));
-        scl[k] = psc[(int64_t)sk * rows_b];
-        o[k] = (f32x4_t){(float)((w2[0] << 16) >> 16), (float)(w2[0] >> 16), (float)((w2[1] << 16) >> 16),
-                         (float)(w2[1] >> 16)};
-      } else {
-        scl[k] = 1.f;
-        o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_b * kDl));
-      }
+      o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_b * kDl));
     }
     float mb = -INFINITY;
 #pragma unroll
@@ -976,12 +993,82 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
     for (int k = 0; k < kBatch; ++k) {
       const float w = s0 + k < ns ? __builtin_amdgcn_exp2f((lz[k] - M) * kLog2e) : 0.f;
       wsum += w;
-      accv += (kCompact ? w * scl[k] : w) * o[k];
+      accv += w * o[k];
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   *(f32x4_t*)(a.out + row * kDl + 4 * d4) = accv * inv;
   if (d4 == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+}
+
+// Combine of compact (int16 + scale) partials: one wave per row; lane l owns
+// dims [8 l, 8 l + 8), one 16-byte load per split. Splits go in batches of 32
+// (one memory round trip for up to 32 splits): every partial load of a batch
+// is issued first, lanes 0..31 fetch the batch's lse and scale values, the
+// batch max and weight sum come from 32-lane reductions, and each split's
+// weight * scale reaches all lanes by readlane.
+// Batches are merged with a running max, as in the fp32 combine.
+__global__ __launch_bounds__(kThreads) void combine_compact_kernel(Args a, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows_b = (int64_t)a.q * kHeads;
+  const int b = (int)(row / rows_b);
+  const int64_t rb = row - (int64_t)b * rows_b;
+  int64_t row0, n;
+  if (!seq_bounds(a, b, row0, n)) {
+    const float nan = __builtin_nanf("");
+    *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){nan, nan, nan, nan};
+    *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){nan, nan, nan, nan};
+    if (lane == 0) a.lse[row] = nan;
+    return;
+  }
+  const int ns = (int)((n + a.chunk - 1) / a.chunk);
+  if (ns <= 1) return;  // the split kernel wrote this row directly
+  const int64_t base = (int64_t)b * a.nsplit * rows_b + rb;  // partial row of split 0
+  const float* pl = a.part_lse + base;
+  const float* psc = a.part_scale + base;
+  const int16_t* pq = a.part_q + base * kDl + 8 * lane;
+  constexpr int kBatch = 32;
+  float M = -INFINITY, wsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+    u32x4_t qv[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int sk = s0 + k < ns ? s0 + k : ns - 1;  // past the end: reload the last (weight 0)
+      qv[k] = __builtin_nontemporal_load((const u32x4_t*)(pq + (int64_t)sk * rows_b * kDl));
+    }
+    const int sl = s0 + (lane & 31);
+    const bool mine = lane < kBatch && sl < ns;
+    const float lz = mine ? pl[(int64_t)sl * rows_b] : -INFINITY;
+    const float sc = mine ? psc[(int64_t)sl * rows_b] : 0.f;
+    const float bmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_max(lz))));
+    if (bmax == -INFINITY) continue;  // every split of this batch is empty (uniform)
+    const float m_new = fmax3(M, bmax);
+    const float r = __builtin_amdgcn_exp2f((M - m_new) * kLog2e);  // 0 while M = -inf
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= r;
+    wsum *= r;
+    M = m_new;
+    const float w = mine ? __builtin_amdgcn_exp2f((lz - M) * kLog2e) : 0.f;
+    wsum += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_sum(w))));
+    const float f = w * sc;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), k));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int32_t v = (int32_t)qv[k][e];
+        acc[2 * e] += fk * (float)((v << 16) >> 16);
+        acc[2 * e + 1] += fk * (float)(v >> 16);
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv;
+  *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv;
+  if (lane == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1121,9 +1208,9 @@ merge:
   if (p.combine) {
     const int64_t rows = (int64_t)a.batch * a.q * kHeads;
     if (compact)
-      hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
+      hipLaunchKernelGGL(combine_compact_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, a, rows);
     else
-      hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
+      hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
     if (hipGetLastError() != hipSuccess) return MLAV_ERR_HIP;
   }
   return MLAV_OK;
@@ -1317,7 +1404,7 @@ int32_t mla_verify_combine(const float* part_out, const float* part_lse, int32_t
   a.nsplit = nsplit;
   a.fixed_ns = nsplit;
   a.chunk = 1;
-  hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0,
                      (hipStream_t)stream, a, rows);
   return hipGetLastError() == hipSuccess ? MLAV_OK : MLAV_ERR_HIP;
 }

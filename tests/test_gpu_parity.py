@@ -285,14 +285,16 @@ def test_compact_partials_within_bound(name):
     row) / 65534 of the fp32 one; the combine takes a convex combination of the
     partials of a row and each partial row is a convex combination of value
     rows, so every output is within max|kv_latent| / 65534 of the fp32-partial
-    output (plus fp32 rounding). The lse does not depend on the stored values."""
+    output (plus fp32 rounding). The lse does not depend on the stored values;
+    the two combine kernels add the split weights in different orders, so it
+    agrees to fp32 reassociation."""
     case = gen.make_workload(name)
     oc, lc = run(case)
     of, lf = run(case, partials=1)
     bound = case.kv_latent.float().abs().max().item() / 65534.0
     diff = (oc - of).abs().max().item()
     assert diff <= bound * 1.01 + 1e-6, f"{name}: compact vs fp32 partials differ by {diff:.3e} > {bound:.3e}"
-    assert torch.equal(lc, lf)
+    assert (lc - lf).abs().max().item() <= 1e-6 * max(1.0, lf.abs().max().item())
     ro, rl = oracle(case) if name != "q9_p65536_chain" else (None, None)
     if ro is not None:
         assert_parity(oc, lc, ro, rl, f"{name} compact partials")
