@@ -47,6 +47,10 @@ def parse():
                     help="after timing, run one device copy of this size (counter calibration)")
     ap.add_argument("--pv-mode", type=int, default=0)
     ap.add_argument("--partials", type=int, default=0, help="0: int16 split partials (default), 1: fp32")
+    ap.add_argument("--paged", action="store_true",
+                    help="read the KV through a page table (one token per page): the rows scattered over a pool "
+                         "by a seeded random permutation, through mla_verify_paged")
+    ap.add_argument("--pool-extra", type=int, default=0, help="paged: pool rows beyond the workload's KV rows")
     return ap.parse_args()
 
 
@@ -54,11 +58,11 @@ def source_digest() -> str:
     return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_counters(workload: str):
+def read_counters(workload: str, paged: bool = False):
     """HBM bytes per split-kernel launch and its MFMA-busy fraction from the
     committed counter summary, or (None, None) when there is none or the
     kernel source changed since."""
-    path = os.path.join(PROFILES, f"split_mfma_kernel_{workload}_counters.txt")
+    path = os.path.join(PROFILES, f"split_mfma_kernel_{workload}{'_paged' if paged else ''}_counters.txt")
     if not os.path.exists(path):
         return None, None
     kv = {}
@@ -128,6 +132,10 @@ def main() -> int:
     ws_bytes = _lib.workspace_size(q, 64, 1, n, n, pv_mode=args.pv_mode, partials=args.partials)
 
     host = {k: getattr(case, k) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
+    if args.paged:
+        pg = gen.make_paged(case, seed=1234, extra_rows=args.pool_extra)
+        host["kv_latent"], host["k_rope"] = pg.pool_latent, pg.pool_rope
+        host["kv_index"] = pg.kv_index
     per_copy = sum(t.numel() * t.element_size() for t in host.values()) + q * 64 * 513 * 4 * (plan.nsplit + 1)
     ncopy = max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))
     copies = []
@@ -143,18 +151,26 @@ def main() -> int:
     # phase 0 = the whole call, 1 = the split kernel alone, 2 = the combine
     # kernel alone (on the workspace phase 1 filled).
     opts = [_lib.options(0, args.pv_mode, 0, args.partials, ph) for ph in range(3)]
+    entry = lib.mla_verify_paged if args.paged else lib.mla_verify_ex
     for d in copies:
-        d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
-                      d["k_rope"].data_ptr(), d["tree_parent"].data_ptr(), p, ctypes.c_float(case.scale),
-                      d["out"].data_ptr(), d["lse"].data_ptr(), q, 64, d["ws"].data_ptr(), ws_bytes,
-                      stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
+        if args.paged:
+            d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
+                          d["k_rope"].data_ptr(), d["kv_index"].data_ptr(), int(d["kv_latent"].shape[0]),
+                          d["tree_parent"].data_ptr(), None, 1, n, n, ctypes.c_float(case.scale),
+                          d["out"].data_ptr(), d["lse"].data_ptr(), q, 64, d["ws"].data_ptr(), ws_bytes,
+                          stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
+        else:
+            d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
+                          d["k_rope"].data_ptr(), d["tree_parent"].data_ptr(), p, ctypes.c_float(case.scale),
+                          d["out"].data_ptr(), d["lse"].data_ptr(), q, 64, d["ws"].data_ptr(), ws_bytes,
+                          stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
     for ph in range(3):
-        rc = lib.mla_verify_ex(*copies[0]["args"][ph])
+        rc = entry(*copies[0]["args"][ph])
         if rc != _lib.MLAV_OK:
-            raise _lib.MLAVError(rc, f"mla_verify_ex (phase {ph})")
+            raise _lib.MLAVError(rc, f"verify call (phase {ph})")
 
     def call(d):
-        lib.mla_verify_ex(*d["args"][0])
+        entry(*d["args"][0])
 
     def warm(fn, rotate: bool = True) -> None:
         # W untimed steps, then more until warmup_ms of wall time has passed
@@ -184,10 +200,10 @@ def main() -> int:
     # each kernel alone: K back-to-back launches (rotating inputs) between two
     # events recorded on the stream the library launches on
     def split(d):
-        lib.mla_verify_ex(*d["args"][1])
+        entry(*d["args"][1])
 
     def merge(d):
-        lib.mla_verify_ex(*d["args"][2])
+        entry(*d["args"][2])
 
     def batch_us(fn) -> float:
         warm(fn)
@@ -242,7 +258,7 @@ def main() -> int:
     tflops = flops / (us_cold * 1e-6) / 1e12
     tflops_warm = flops / (us_warm * 1e-6) / 1e12
     achieved = flops / (split_us * 1e-6) / 1e12
-    traffic, mfma_busy = read_counters(args.workload)
+    traffic, mfma_busy = read_counters(args.workload, args.paged)
     res = {
         "metric": "MLA verify attention us/call + TFLOP/s (% MFMA peak), H=64 q_len=9, prefix 16k",
         "value": round(tflops, 2),
@@ -260,6 +276,8 @@ def main() -> int:
         "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": n, "heads": 64, "dl": 512,
                    "dr": 64, "tree": case.meta["tree"], "scale": case.scale, "nsplit": plan.nsplit,
                    "chunk": plan.chunk, "pv_mode": args.pv_mode, "partials": "int16" if args.partials == 0 else "fp32",
+                   "kv_layout": (f"paged, one token per page, pool {n + args.pool_extra} rows" if args.paged
+                                 else "contiguous"),
                    "parallelism": "single GPU"},
         "us_per_call": round(us_cold, 2),
         "us_per_call_warm": round(us_warm, 2),

@@ -70,6 +70,8 @@ extern "C" {
 #define MLAV_DR 64       /* rope width */
 #define MLAV_MAX_KV 4000000 /* KV rows per sequence (byte offsets into one sequence's
                                latent rows must stay below 2^32) */
+#define MLAV_MAX_POOL 4000000 /* rows of a paged KV pool (byte offsets into the pool's
+                                 latent rows must stay below 2^32) */
 
 /* Tuning knobs; a NULL options pointer means all zeros. */
 typedef struct mlav_options {
@@ -147,6 +149,33 @@ int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, cons
                            int64_t max_kv, float scale, float* out, float* lse, int32_t q_len,
                            int32_t num_heads, void* workspace, size_t workspace_bytes,
                            void* stream, const mlav_options* opt);
+
+/*
+ * Paged KV with one token per page (the layout of a serving KV pool whose
+ * page size is 1: page "The Moment of Truth", section "Output Knowledge
+ * Created", and page "The Validation Milestone", the Triton-baseline
+ * paragraph, where it makes the attention a scattered gather). The keys and
+ * values live in a pool of pool_rows rows, and a page table maps each
+ * sequence's logical KV rows (its prefix, then its q_len tree tokens) to pool
+ * rows; otherwise the operation is the one above.
+ *   kv_latent [pool_rows, 512], k_rope [pool_rows, 64] bf16   the pool
+ *   kv_index  [total_kv] int32 DEVICE: logical row -> pool row; an entry
+ *             outside [0, pool_rows) reads as a row of zeros (never out of
+ *             bounds)
+ *   pool_rows 1 .. MLAV_MAX_POOL
+ *   kv_offsets [batch + 1] int64 DEVICE: sequence b owns logical rows
+ *             [kv_offsets[b], kv_offsets[b+1]) of kv_index; may be NULL for a
+ *             single sequence (batch = 1, max_kv = total_kv = its row count)
+ *   q_nope_absorbed, q_rope, tree_parent, out, lse: as mla_verify_batched
+ * The page-table entries are read on the device; the kernels stay in bounds
+ * for any entries. Workspace: as mla_verify_batched.
+ */
+int32_t mla_verify_paged(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                         const void* k_rope, const int32_t* kv_index, int64_t pool_rows,
+                         const int32_t* tree_parent, const int64_t* kv_offsets, int32_t batch,
+                         int64_t total_kv, int64_t max_kv, float scale, float* out, float* lse,
+                         int32_t q_len, int32_t num_heads, void* workspace, size_t workspace_bytes,
+                         void* stream, const mlav_options* opt);
 
 /* Workspace bytes a call with these sizes and options needs (0 when no split
    is needed); it depends on opt->partials.

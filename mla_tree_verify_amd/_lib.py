@@ -27,6 +27,7 @@ EXPORTS = (
     "mla_verify",
     "mla_verify_ex",
     "mla_verify_batched",
+    "mla_verify_paged",
     "mla_verify_partials",
     "mla_verify_workspace_size",
     "mla_verify_plan",
@@ -74,6 +75,10 @@ def load():
                                                  c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
                                                  c_void_p, POINTER(Options)]
     lib.mla_verify_batched.restype = c_int32
+    lib.mla_verify_paged.argtypes = tensors + [c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_int64, c_int64,
+                                               c_float, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
+                                               c_void_p, POINTER(Options)]
+    lib.mla_verify_paged.restype = c_int32
     lib.mla_verify_partials.argtypes = tensors + [c_void_p, c_int64, c_float, c_void_p, c_void_p, c_int32,
                                                   c_int32, POINTER(Plan), c_void_p, POINTER(Options)]
     lib.mla_verify_partials.restype = c_int32

@@ -123,6 +123,66 @@ def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: to
     return out, lse
 
 
+def mla_verify_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, pool_latent: torch.Tensor,
+                     pool_rope: torch.Tensor, kv_index: torch.Tensor, tree_parent: torch.Tensor, scale: float,
+                     kv_offsets: Optional[torch.Tensor] = None, max_kv: Optional[int] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, nsplit: int = 0, pv_mode: int = 0,
+                     kernel: int = 0, partials: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged KV (one token per page): pool_latent [R,512], pool_rope [R,64] bf16,
+    kv_index [N] int32 (logical row -> pool row). One sequence: q_nope [q,H,512],
+    tree_parent [q], kv_offsets None (its N logical rows are its prefix then its
+    tree). Batch: q_nope [B,q,H,512], tree_parent [B,q], kv_offsets [B+1] int64."""
+    if not q_nope.is_cuda:
+        raise ValueError("inputs must be on a GPU (the library has no CPU path)")
+    dev = q_nope.device
+    batched = kv_offsets is not None
+    if batched:
+        bsz, q, h = int(q_nope.shape[0]), int(q_nope.shape[1]), int(q_nope.shape[2])
+    else:
+        bsz, (q, h) = 1, (int(q_nope.shape[0]), int(q_nope.shape[1]))
+    total = int(kv_index.shape[0])
+    pool = int(pool_latent.shape[0])
+    lead = (bsz,) if batched else ()
+    _check(q_nope, "q_nope", torch.bfloat16, lead + (q, h, DL), dev)
+    _check(q_rope, "q_rope", torch.bfloat16, lead + (q, h, DR), dev)
+    _check(pool_latent, "pool_latent", torch.bfloat16, (pool, DL), dev)
+    _check(pool_rope, "pool_rope", torch.bfloat16, (pool, DR), dev)
+    _check(kv_index, "kv_index", torch.int32, (total,), dev)
+    _check(tree_parent, "tree_parent", torch.int32, lead + (q,), dev)
+    offs_ptr = None
+    if batched:
+        if kv_offsets.dtype != torch.int64 or tuple(kv_offsets.shape) != (bsz + 1,):
+            raise ValueError("kv_offsets must be int64 [B+1]")
+        if max_kv is None:
+            host = kv_offsets.detach().cpu()
+            max_kv = int((host[1:] - host[:-1]).max().item())
+        kv_offsets = kv_offsets.to(dev) if not kv_offsets.is_cuda else kv_offsets
+        offs_ptr = kv_offsets.data_ptr()
+    else:
+        max_kv = total
+    if out is None:
+        out = torch.empty(lead + (q, h, DL), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(lead + (q, h), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, lead + (q, h, DL), dev)
+    _check(lse, "lse", torch.float32, lead + (q, h), dev)
+    lib = _lib.load()
+    opt = _lib.options(nsplit, pv_mode, kernel, partials)
+    need = int(lib.mla_verify_workspace_size(q, h, bsz, total, int(max_kv), 0, ctypes.byref(opt)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.mla_verify_paged(q_nope.data_ptr(), q_rope.data_ptr(), pool_latent.data_ptr(), pool_rope.data_ptr(),
+                              kv_index.data_ptr(), pool, tree_parent.data_ptr(), offs_ptr, bsz, total,
+                              int(max_kv), float(scale), out.data_ptr(), lse.data_ptr(), q, h, ws_ptr, ws_bytes,
+                              _stream_ptr(dev), ctypes.byref(opt))
+    if rc != _lib.MLAV_OK:
+        raise _lib.MLAVError(rc, "mla_verify_paged")
+    return out, lse
+
+
 def mla_verify_partials(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tensor,
                         k_rope: torch.Tensor, tree_parent: torch.Tensor, prefix_len: int, scale: float,
                         plan: _lib.Plan, part_out: Optional[torch.Tensor] = None,

@@ -90,6 +90,8 @@ struct Args {
   const uint16_t* rope;  // [total, 64]
   const int32_t* parent; // [B, q]
   const int64_t* offs;   // [B + 1] or null (one sequence of single_n rows)
+  const int32_t* idx;    // paged KV: [total] logical row -> row of the lat/rope pool; null = contiguous
+  int64_t pool_rows;     // paged KV: rows of the pool
   float* out;            // [B, q, H, 512]
   float* lse;            // [B, q, H]
   float* part_o;         // [B, S, q, H, 512] fp32 partials
@@ -318,6 +320,27 @@ __device__ inline void issue_tile(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_r
     issue_tile_part(buf, lat_rs, rope_rs, key_rel, wave, lane, rope_voff, part);
 }
 
+// Paged KV (one token per page): the same tile layout, gathered through a
+// page table. idx_lane holds, in lane j < 32, the pool row of key j of the
+// tile (-1: none, the slot gets zeros); rope_idx is the pool row of this
+// lane's rope row 8 wave + (lane>>3). A latent row is one whole instruction,
+// so its pool row is wave-uniform (readlane); the descriptors span the pool
+// and a row outside it reads zeros.
+__device__ inline void issue_tile_part_paged(LDS_AS char* buf, __amdgpu_buffer_rsrc_t lat_rs,
+                                             __amdgpu_buffer_rsrc_t rope_rs, int idx_lane, int rope_idx,
+                                             int wave, int lane, int rope_loff, int part) {
+  if (part < 8) {
+    const int k = 4 * part + wave;
+    const int prow = __builtin_amdgcn_readlane(idx_lane, k);
+    const uint32_t off = prow >= 0 ? (uint32_t)prow * 1024u + 16u * (uint32_t)(lane ^ swz(k)) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rs, (LDS_AS void*)(buf + k * 1024), 16, (int)off, 0, 0, 0);
+  } else {
+    const uint32_t off = rope_idx >= 0 ? (uint32_t)rope_idx * 128u + (uint32_t)rope_loff : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rs, (LDS_AS void*)(buf + kLatBytes + wave * 1024), 16,
+                                             (int)off, 0, 0, 0);
+  }
+}
+
 // Lane bases of the K operand reads. Score k-step ks of a wave reads 16-byte
 // chunk c = 36 kDh + 2 ks + (lane>>5) of key lane&31's 576-d row (chunks
 // 0..63 latent, 64..71 rope). A latent chunk is stored at position
@@ -399,7 +422,7 @@ __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&
 // tile load into one slot does not write the slots being read and issues no
 // wait for it), an 8 KB partial-score exchange and an 8 KB weight exchange:
 // 163840 bytes. A tile is loaded three steps ahead of its value product.
-template <int kDh, bool kHiLo, bool kCompact>
+template <int kDh, bool kHiLo, bool kCompact, bool kPaged>
 __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r1, LDS_AS char* r2,
                                   LDS_AS char* r3, LDS_AS char* xs, LDS_AS char* xp, int b, int s,
                                   int t, int wave, int hh, int lane, int64_t row0, int64_t n) {
@@ -420,27 +443,67 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   // tree, then tiles 1 and 2, so that load latency overlaps the ancestor
   // walk and the wait before the first scores covers tile 0 and the queries
   // only (loads complete in issue order).
+  // contiguous KV: descriptors over this chunk's rows onward; paged KV: over the pool
   const __amdgpu_buffer_rsrc_t lat_rs =
-      make_rsrc(a.lat + (row0 + c0) * kDl, (uint32_t)(n32 - c0) * (kDl * 2));
+      kPaged ? make_rsrc(a.lat, (uint32_t)a.pool_rows * (kDl * 2))
+             : make_rsrc(a.lat + (row0 + c0) * kDl, (uint32_t)(n32 - c0) * (kDl * 2));
   const __amdgpu_buffer_rsrc_t rope_rs =
-      make_rsrc(a.rope + (row0 + c0) * kDr, (uint32_t)(n32 - c0) * (kDr * 2));
+      kPaged ? make_rsrc(a.rope, (uint32_t)a.pool_rows * (kDr * 2))
+             : make_rsrc(a.rope + (row0 + c0) * kDr, (uint32_t)(n32 - c0) * (kDr * 2));
   // rope row 8 wave + (lane>>3) of a tile: LDS position lane&7 holds
   // logical chunk (lane&7) ^ swz_rope(row)
-  const int rope_voff = (lane >> 3) * 128 + 16 * ((lane & 7) ^ swz_rope(8 * wave + (lane >> 3)));
+  const int rope_loff = 16 * ((lane & 7) ^ swz_rope(8 * wave + (lane >> 3)));
+  const int rope_voff = (lane >> 3) * 128 + rope_loff;
   // every step issues nine loads (tiles past the chunk end request nothing)
-  // so that vmcnt(9) always means "all but the latest tile landed"
+  // so that vmcnt(9) always means "all but the latest tile landed"; paged KV
+  // adds one page-table load per step (issued before the step's tile loads),
+  // so its count is 10
   auto tile_rel = [&](int i) { return i < ntiles ? i * kTile : kNoTile; };
-  auto issue_next_tiles = [&]() {
-    issue_tile(r1, lat_rs, rope_rs, tile_rel(1), wave, lane, rope_voff);
-    issue_tile(r2, lat_rs, rope_rs, tile_rel(2), wave, lane, rope_voff);
+  // page-table entries of tile i: every lane loads from a valid address (so
+  // this is exactly one load instruction); the raw entries are checked only
+  // when used, a step later, so that nothing waits for the load early
+  auto idx_valid = [&](int i) {
+    const int L = c0 + i * kTile + (lane & 31);
+    return lane < 32 && i < ntiles && L < c1;
   };
-  issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+  auto load_idx = [&](int i) -> int {
+    return a.idx[row0 + (idx_valid(i) ? c0 + i * kTile + (lane & 31) : c0)];
+  };
+  // lane j < 32: the pool row of key j of tile i, -1 past the chunk or outside the pool
+  auto checked_idx = [&](int i, int raw) { return idx_valid(i) && raw >= 0 && raw < a.pool_rows ? raw : -1; };
+  auto rope_rows = [&](int idx_lane) { return __shfl(idx_lane, 8 * wave + (lane >> 3), 64); };
+  auto issue_paged = [&](LDS_AS char* buf, int idx_lane) {
+    const int ri = rope_rows(idx_lane);
+#pragma unroll
+    for (int part = 0; part < 9; ++part)
+      issue_tile_part_paged(buf, lat_rs, rope_rs, idx_lane, ri, wave, lane, rope_loff, part);
+  };
+  int idx_cur = -1;  // paged: raw page-table entries of the next tile to load
+  // the first three tiles; paged KV reads their page-table entries first and
+  // the fourth tile's between tiles 1 and 2 (the same ten loads as a step)
+  auto first_tiles = [&](auto&& between) {
+    if constexpr (kPaged) {
+      const int i0 = load_idx(0), i1 = load_idx(1), i2 = load_idx(2);
+      issue_paged(r0, checked_idx(0, i0));
+      between();
+      issue_paged(r1, checked_idx(1, i1));
+      __builtin_amdgcn_sched_barrier(0);
+      idx_cur = load_idx(3);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_paged(r2, checked_idx(2, i2));
+    } else {
+      issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+      between();
+      issue_tile(r1, lat_rs, rope_rs, tile_rel(1), wave, lane, rope_voff);
+      issue_tile(r2, lat_rs, rope_rs, tile_rel(2), wave, lane, rope_voff);
+    }
+  };
 
-  const int par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
-
+  int par_lane;
   // resident queries for this wave's dim half: B operand of S^T = K Q^T
   bf16x8_t qreg[18];
-  {
+  first_tiles([&]() {
+    par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
     const int64_t qrow = ((int64_t)b * a.q + t) * kHeads + head;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
@@ -448,7 +511,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       qreg[ks] = d < kDl ? *(const bf16x8_t*)(a.qn + qrow * kDl + d)
                          : *(const bf16x8_t*)(a.qr + qrow * kDr + (d - kDl));
     }
-  }
+  });
 
   // V^T operand (transposing reads): in each 16-lane group lane i reads 4
   // dims (16 dhalf + 4 (i&3) ..) of key row kk = 4 half + (i>>2) (+8 v for
@@ -466,7 +529,6 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     for (int m = 0; m < 4; ++m) vb[m] = kk * 1024 + 16 * (z0 ^ (4 * m)) + 8 * (i & 1);
   }
 
-  issue_next_tiles();
   const uint64_t anc = ancestor_mask_wave(par_lane, a.q, t);
 
   const int partner = wave ^ 1;  // same head half, other dim half
@@ -504,11 +566,12 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // prologue: tiles 0..2 in flight; tile 0's partial scores exchanged in
     // full (through ring slot 3, free until tile 3 is loaded) to fix m_ref,
     // then its partner half published for step 0
-    if (attempt == 1) {
-      issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
-      issue_next_tiles();
-    }
-    __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18): tile 0 landed (tiles 1, 2 may be in flight)
+    if (attempt == 1) first_tiles([]() {});
+    // tile 0 landed; tiles 1, 2 (and the fourth tile's page-table entries) may be in flight
+    if (kPaged)
+      __builtin_amdgcn_s_waitcnt(0x4F73);  // vmcnt(19)
+    else
+      __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18)
     __syncthreads();
     const f32x16_t s0 = tile_scores<kDh>(r0, qreg, kb);
     float own[8];  // this wave's elements of the next tile's partial scores
@@ -662,6 +725,15 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
           (f32x4_t){sc[kSend + 4], sc[kSend + 5], sc[kSend + 6], sc[kSend + 7]};
       __builtin_amdgcn_sched_barrier(0);
 
+      // paged KV: this step's loads use the page-table entries read one step
+      // ago; the next tile's entries are requested before them
+      int idx_dma = 0, rope_dma = 0, idx_next = 0;
+      if constexpr (kPaged) {
+        idx_dma = checked_idx(i + 3, idx_cur);
+        rope_dma = rope_rows(idx_dma);
+        idx_next = load_idx(i + 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // values of tile i; tile loads in the first slots (each slot holds two
       // MFMAs, so it has issue room to spare)
 #pragma unroll
@@ -673,18 +745,27 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
           acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], __builtin_bit_cast(bf16x8_t, pl[j >> 3]),
                                                                acc[j & 7], 0, 0, 0);
         if (nn + kAhead < 16) vf[frag(nn + kAhead)] = vread(frag(nn + kAhead));
-        if (nn < 9) issue_tile_part(dma_buf, lat_rs, rope_rs, dma_rel, wave, lane, rope_voff, nn);
+        if (kPaged) {
+          if (nn < 9) issue_tile_part_paged(dma_buf, lat_rs, rope_rs, idx_dma, rope_dma, wave, lane, rope_loff, nn);
+        } else {
+          if (nn < 9) issue_tile_part(dma_buf, lat_rs, rope_rs, dma_rel, wave, lane, rope_voff, nn);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) own[k] = sc[kOwn + k];
+      if constexpr (kPaged) idx_cur = idx_next;
     };
 
     // Tile i+1 landed (tile i+2 may still be in flight) and the partner
     // scores of tile i are published once every wave passes the barrier;
     // ring slot (i+3)%4 is free from then on.
     auto advance = [&](int) {
-      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): only tile i+2's loads may be outstanding
+      // only tile i+2's loads (and, paged, the page-table load before them) may be outstanding
+      if (kPaged)
+        __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
       lds_barrier();
     };
     // Tiles wholly inside the prefix and the chunk need no mask. Their loop
@@ -832,7 +913,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   }
 }
 
-template <bool kHiLo, bool kCompact>
+template <bool kHiLo, bool kCompact, bool kPaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_mfma_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char ring0[kTileBytes];
@@ -867,9 +948,9 @@ void split_mfma_kernel(Args a) {
   if ((int64_t)s * a.chunk >= n) return;  // this sequence needs fewer splits
   const int hh = wave >> 1;
   if ((wave & 1) == 0)
-    split_body<0, kHiLo, kCompact>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
+    split_body<0, kHiLo, kCompact, kPaged>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
   else
-    split_body<1, kHiLo, kCompact>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
+    split_body<1, kHiLo, kCompact, kPaged>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -906,14 +987,23 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(Args a) {
   float m = -INFINITY, l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int64_t j = c0; j < c1; ++j) {
     if (!key_visible(j, c1, prefix, anc)) continue;
-    const uint16_t* kl = a.lat + (row0 + j) * kDl + 8 * lane;
+    // contiguous KV: row row0 + j; paged KV: the pool row the page table
+    // gives, a row outside the pool reading as zeros (as in the MFMA kernel)
+    int64_t krow = row0 + j;
+    bool zero = false;
+    if (a.idx) {
+      const int pr = a.idx[row0 + j];
+      zero = pr < 0 || pr >= a.pool_rows;
+      krow = zero ? 0 : pr;
+    }
+    const uint16_t* kl = a.lat + krow * kDl + 8 * lane;
     float v[8];
     float part = 0.f;
     for (int d = 0; d < 8; ++d) {
-      v[d] = bf16_to_f32(kl[d]);
+      v[d] = zero ? 0.f : bf16_to_f32(kl[d]);
       part += qv[d] * v[d];
     }
-    part += qv[8] * bf16_to_f32(a.rope[(row0 + j) * kDr + lane]);
+    part += qv[8] * (zero ? 0.f : bf16_to_f32(a.rope[krow * kDr + lane]));
     for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
     const float sj = part * a.scale_log2;
     const float m_new = fmax3(m, sj);
@@ -1188,17 +1278,15 @@ int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* 
   const int phase = opt ? opt->phase : 0;
   if (phase == 2) goto merge;
   if (kernel == 0) {
-    if (pv_mode == 0) {
-      if (compact)
-        hipLaunchKernelGGL((split_mfma_kernel<true, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
-      else
-        hipLaunchKernelGGL((split_mfma_kernel<true, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
-    } else {
-      if (compact)
-        hipLaunchKernelGGL((split_mfma_kernel<false, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
-      else
-        hipLaunchKernelGGL((split_mfma_kernel<false, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
-    }
+    // one instantiation per (weight form, partial format, KV layout)
+    using K = void (*)(Args);
+    static const K table[2][2][2] = {
+        {{split_mfma_kernel<true, false, false>, split_mfma_kernel<true, false, true>},
+         {split_mfma_kernel<true, true, false>, split_mfma_kernel<true, true, true>}},
+        {{split_mfma_kernel<false, false, false>, split_mfma_kernel<false, false, true>},
+         {split_mfma_kernel<false, true, false>, split_mfma_kernel<false, true, true>}}};
+    const K k = table[pv_mode == 0 ? 0 : 1][compact ? 1 : 0][a.idx ? 1 : 0];
+    hipLaunchKernelGGL(k, dim3(p.grid), dim3(kThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL(split_valu_kernel, dim3(p.grid), dim3(kThreads), 0, st, a);
   }
@@ -1331,6 +1419,56 @@ int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, cons
   a.lse = lse;
   set_partials(a, workspace, p, q_len, batch, compact);
   a.single_n = 0;
+  a.total_kv = total_kv;
+  a.max_kv = max_kv;
+  a.scale_log2 = scale * kLog2e;
+  a.q = q_len;
+  a.batch = batch;
+  return launch(a, p, opt, stream);
+}
+
+int32_t mla_verify_paged(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                         const void* k_rope, const int32_t* kv_index, int64_t pool_rows,
+                         const int32_t* tree_parent, const int64_t* kv_offsets, int32_t batch,
+                         int64_t total_kv, int64_t max_kv, float scale, float* out, float* lse,
+                         int32_t q_len, int32_t num_heads, void* workspace, size_t workspace_bytes,
+                         void* stream, const mlav_options* opt) {
+  int rc = common_checks(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, scale, out, lse,
+                         q_len, num_heads, opt);
+  if (rc != MLAV_OK) return rc;
+  if (!kv_index) return MLAV_ERR_NULL;
+  if (!aligned(kv_index, 4)) return MLAV_ERR_ALIGN;
+  if (pool_rows < 1 || pool_rows > MLAV_MAX_POOL) return MLAV_ERR_SHAPE;
+  if (batch < 1 || max_kv < q_len || total_kv < (int64_t)batch * q_len || max_kv > total_kv)
+    return MLAV_ERR_SHAPE;
+  if (kv_offsets) {
+    if (!aligned(kv_offsets, 8)) return MLAV_ERR_ALIGN;
+  } else if (batch != 1 || max_kv != total_kv) {
+    return MLAV_ERR_ARG;  // without offsets there is one sequence of total_kv rows
+  }
+  int32_t cus = 0;
+  rc = device_cus(&cus);
+  if (rc != MLAV_OK) return rc;
+  mlav_plan p;
+  rc = plan_impl(q_len, num_heads, batch, total_kv, max_kv, cus, opt, &p);
+  if (rc != MLAV_OK) return rc;
+  const bool compact = compact_partials(opt);
+  const size_t need = workspace_bytes_for(p, q_len, batch, compact);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
+  Args a{};
+  a.qn = (const uint16_t*)q_nope_absorbed;
+  a.qr = (const uint16_t*)q_rope;
+  a.lat = (const uint16_t*)kv_latent;
+  a.rope = (const uint16_t*)k_rope;
+  a.parent = tree_parent;
+  a.offs = kv_offsets;
+  a.idx = kv_index;
+  a.pool_rows = pool_rows;
+  a.out = out;
+  a.lse = lse;
+  set_partials(a, workspace, p, q_len, batch, compact);
+  a.single_n = kv_offsets ? 0 : total_kv;
   a.total_kv = total_kv;
   a.max_kv = max_kv;
   a.scale_log2 = scale * kLog2e;

@@ -216,6 +216,31 @@ def make_batched_case(
     )
 
 
+@dataclass
+class Paged:
+    """The KV rows of a case scattered over a larger pool (one token per page)."""
+
+    pool_latent: torch.Tensor  # bf16 [pool_rows, Dl]
+    pool_rope: torch.Tensor  # bf16 [pool_rows, Dr]
+    kv_index: torch.Tensor  # int32 [N]: logical row -> pool row
+
+
+def make_paged(case: Case, seed: int, extra_rows: int = 0, garbage: float = 100.0) -> Paged:
+    """Scatter the case's N logical KV rows over a pool of N + extra_rows rows by
+    a seeded random permutation; pool rows no logical row maps to hold large
+    random values (garbage that must never be read)."""
+    g = torch.Generator().manual_seed(seed)
+    n = int(case.kv_latent.shape[0])
+    pool_rows = n + extra_rows
+    perm = torch.randperm(pool_rows, generator=g)[:n]
+    dl, dr = int(case.kv_latent.shape[1]), int(case.k_rope.shape[1])
+    pool_latent = (torch.randn(pool_rows, dl, generator=g) * garbage).to(torch.bfloat16)
+    pool_rope = (torch.randn(pool_rows, dr, generator=g) * garbage).to(torch.bfloat16)
+    pool_latent[perm] = case.kv_latent
+    pool_rope[perm] = case.k_rope
+    return Paged(pool_latent=pool_latent, pool_rope=pool_rope, kv_index=perm.to(torch.int32))
+
+
 # --------------------------------------------------------------------------
 # the named workloads (sizes as the benchmark tables on the pages use them)
 # --------------------------------------------------------------------------

@@ -153,6 +153,33 @@ def mla_verify_batched(q_nope, q_rope, kv_latent, k_rope, tree_parent, kv_offset
     return np.stack(outs), np.stack(lses)
 
 
+def gather_pages(pool_latent, pool_rope, kv_index) -> Tuple[np.ndarray, np.ndarray]:
+    """Paged KV with one token per page: logical KV row r is row kv_index[r]
+    of the pool (page "The Moment of Truth", section "Output Knowledge
+    Created": the serving cache uses page_size=1, so attention gathers scattered
+    rows). An entry outside [0, pool_rows) is read as a row of zeros (this
+    library's reading; the pages do not say). Returns the logical rows in
+    order, float64."""
+    lat, rope = to_f64(pool_latent), to_f64(pool_rope)
+    idx = np.asarray(to_f64(kv_index)).astype(np.int64).reshape(-1)
+    ok = (idx >= 0) & (idx < lat.shape[0])
+    safe = np.where(ok, idx, 0)
+    g_lat = np.where(ok[:, None], lat[safe], 0.0)
+    g_rope = np.where(ok[:, None], rope[safe], 0.0)
+    return g_lat, g_rope
+
+
+def mla_verify_paged(q_nope, q_rope, pool_latent, pool_rope, kv_index, tree_parent, scale: float,
+                     prefix_len: int = None, kv_offsets=None) -> Tuple[np.ndarray, np.ndarray]:
+    """The verify step over a paged KV pool: gather the logical rows through
+    the page table, then the plain definition. One sequence (prefix_len) or a
+    batch (kv_offsets into the logical rows, as mla_verify_batched)."""
+    lat, rope = gather_pages(pool_latent, pool_rope, kv_index)
+    if kv_offsets is None:
+        return mla_verify(q_nope, q_rope, lat, rope, tree_parent, prefix_len, scale)
+    return mla_verify_batched(q_nope, q_rope, lat, rope, tree_parent, kv_offsets, scale)
+
+
 # --------------------------------------------------------------------------
 # the combine formula for KV-split partials
 # --------------------------------------------------------------------------

@@ -168,3 +168,26 @@ def test_combine_validation(lib):
     assert f(A, A, 0, 64, A, A, None) == _lib.MLAV_ERR_SHAPE
     assert f(A, A, 2, 63, A, A, None) == _lib.MLAV_ERR_SHAPE
     assert f(A + 4, A, 2, 64, A, A, None) == _lib.MLAV_ERR_ALIGN
+
+
+def test_paged_validation_errors(lib):
+    opt = _lib.options()
+    f = lib.mla_verify_paged
+    ok = dict(idx=A, pool=1000, offs=None, batch=1, total=300, maxkv=300)
+
+    def c(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return f(A, A, A, A, d["idx"], d["pool"], A, d["offs"], d["batch"], d["total"], d["maxkv"], 0.07, A, A,
+                 9, 64, None, 0, None, ctypes.byref(opt))
+
+    assert c(idx=None) == _lib.MLAV_ERR_NULL
+    assert c(idx=A + 2) == _lib.MLAV_ERR_ALIGN
+    assert c(pool=0) == _lib.MLAV_ERR_SHAPE
+    assert c(pool=4000001) == _lib.MLAV_ERR_SHAPE
+    assert c(batch=0) == _lib.MLAV_ERR_SHAPE
+    assert c(total=5, maxkv=5) == _lib.MLAV_ERR_SHAPE
+    # without offsets there is exactly one sequence of total_kv rows
+    assert c(batch=2, total=600, maxkv=300) == _lib.MLAV_ERR_ARG
+    assert c(maxkv=200) == _lib.MLAV_ERR_ARG
+    assert c(offs=A + 4, batch=2, total=600, maxkv=300) == _lib.MLAV_ERR_ALIGN

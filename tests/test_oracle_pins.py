@@ -433,3 +433,40 @@ def test_pins_catch_planted_mistakes(name, monkeypatch):
     except Exception:
         caught = True  # a crash is also a detection
     assert caught, f"planted mistake {name!r} slipped through every pin"
+
+
+# ---------------------------------------------------------------------------
+# paged KV: the gather through the page table
+# ---------------------------------------------------------------------------
+def test_paged_oracle_equals_contiguous_oracle():
+    """Scattering the KV rows over a larger pool of garbage rows and reading
+    them back through the page table gives exactly the contiguous result."""
+    case = gen.make_case(5, 40, tree="random", seed=71, num_heads=4, dl=16, dr=4)
+    pg = gen.make_paged(case, seed=72, extra_rows=25)
+    ro, rl = orc.mla_verify(case.q_nope, case.q_rope, case.kv_latent, case.k_rope, case.tree_parent,
+                            case.prefix_len, case.scale)
+    po, pl = orc.mla_verify_paged(case.q_nope, case.q_rope, pg.pool_latent, pg.pool_rope, pg.kv_index,
+                                  case.tree_parent, case.scale, prefix_len=case.prefix_len)
+    assert np.array_equal(po, ro) and np.array_equal(pl, rl)
+
+
+def test_paged_oracle_out_of_pool_entry_is_a_zero_row():
+    case = gen.make_case(3, 10, tree="chain", seed=73, num_heads=2, dl=8, dr=2)
+    pg = gen.make_paged(case, seed=74, extra_rows=5)
+    idx = pg.kv_index.clone()
+    idx[4] = -1
+    idx[7] = pg.pool_latent.shape[0] + 3
+    zeroed = gen.make_case(3, 10, tree="chain", seed=73, num_heads=2, dl=8, dr=2)
+    zeroed.kv_latent[4] = 0
+    zeroed.kv_latent[7] = 0
+    zeroed.k_rope[4] = 0
+    zeroed.k_rope[7] = 0
+    ro, rl = orc.mla_verify(zeroed.q_nope, zeroed.q_rope, zeroed.kv_latent, zeroed.k_rope, zeroed.tree_parent,
+                            10, zeroed.scale)
+    po, pl = orc.mla_verify_paged(case.q_nope, case.q_rope, pg.pool_latent, pg.pool_rope, idx, case.tree_parent,
+                                  case.scale, prefix_len=10)
+    assert np.array_equal(po, ro) and np.array_equal(pl, rl)
+    # a zero key still counts (score 0): the lse differs from dropping the row
+    dropped = orc.mla_verify(case.q_nope, case.q_rope, np.delete(orc.to_f64(case.kv_latent), [4, 7], 0),
+                             np.delete(orc.to_f64(case.k_rope), [4, 7], 0), case.tree_parent, 8, case.scale)
+    assert not np.allclose(dropped[1], pl)
