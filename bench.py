@@ -51,6 +51,8 @@ def parse():
                     help="read the KV through a page table (one token per page): the rows scattered over a pool "
                          "by a seeded random permutation, through mla_verify_paged")
     ap.add_argument("--pool-extra", type=int, default=0, help="paged: pool rows beyond the workload's KV rows")
+    ap.add_argument("--heads", type=int, default=64,
+                    help="query heads per token (the workload's shape with this head count; 64 is the metric's)")
     return ap.parse_args()
 
 
@@ -122,27 +124,33 @@ def main() -> int:
     if spec["kind"] != "single":
         print(json.dumps({"error": "bench.py times single-sequence workloads"}))
         return 2
-    case = gen.make_workload(args.workload)
+    if args.heads == 64:
+        case = gen.make_workload(args.workload)
+    else:
+        kw = dict(gen.WORKLOADS[args.workload])
+        kw.pop("kind")
+        case = gen.make_case(num_heads=args.heads, **kw)
     q, p = case.q_len, case.prefix_len
     n = p + q
-    flops = orc.algorithmic_flops(case.tree_parent, p)
-    alg_bytes = orc.algorithmic_bytes(q, n)
-    plan = api.device_plan(q, 1, n, n, pv_mode=args.pv_mode)
+    H = args.heads
+    flops = orc.algorithmic_flops(case.tree_parent, p, num_heads=H)
+    alg_bytes = orc.algorithmic_bytes(q, n, num_heads=H)
+    plan = api.device_plan(q, 1, n, n, pv_mode=args.pv_mode, num_heads=H)
     lib = _lib.load()
-    ws_bytes = _lib.workspace_size(q, 64, 1, n, n, pv_mode=args.pv_mode, partials=args.partials)
+    ws_bytes = _lib.workspace_size(q, H, 1, n, n, pv_mode=args.pv_mode, partials=args.partials)
 
     host = {k: getattr(case, k) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
     if args.paged:
         pg = gen.make_paged(case, seed=1234, extra_rows=args.pool_extra)
         host["kv_latent"], host["k_rope"] = pg.pool_latent, pg.pool_rope
         host["kv_index"] = pg.kv_index
-    per_copy = sum(t.numel() * t.element_size() for t in host.values()) + q * 64 * 513 * 4 * (plan.nsplit + 1)
+    per_copy = sum(t.numel() * t.element_size() for t in host.values()) + ws_bytes + q * H * 513 * 4
     ncopy = max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))
     copies = []
     for _ in range(ncopy):
         d = {k: v.to(dev) for k, v in host.items()}
-        d["out"] = torch.empty(q, 64, 512, dtype=torch.float32, device=dev)
-        d["lse"] = torch.empty(q, 64, dtype=torch.float32, device=dev)
+        d["out"] = torch.empty(q, H, 512, dtype=torch.float32, device=dev)
+        d["lse"] = torch.empty(q, H, dtype=torch.float32, device=dev)
         d["ws"] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         copies.append(d)
     stream = torch.cuda.current_stream(dev)
@@ -157,12 +165,12 @@ def main() -> int:
             d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
                           d["k_rope"].data_ptr(), d["kv_index"].data_ptr(), int(d["kv_latent"].shape[0]),
                           d["tree_parent"].data_ptr(), None, 1, n, n, ctypes.c_float(case.scale),
-                          d["out"].data_ptr(), d["lse"].data_ptr(), q, 64, d["ws"].data_ptr(), ws_bytes,
+                          d["out"].data_ptr(), d["lse"].data_ptr(), q, H, d["ws"].data_ptr(), ws_bytes,
                           stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
         else:
             d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
                           d["k_rope"].data_ptr(), d["tree_parent"].data_ptr(), p, ctypes.c_float(case.scale),
-                          d["out"].data_ptr(), d["lse"].data_ptr(), q, 64, d["ws"].data_ptr(), ws_bytes,
+                          d["out"].data_ptr(), d["lse"].data_ptr(), q, H, d["ws"].data_ptr(), ws_bytes,
                           stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
     for ph in range(3):
         rc = entry(*copies[0]["args"][ph])
@@ -258,7 +266,7 @@ def main() -> int:
     tflops = flops / (us_cold * 1e-6) / 1e12
     tflops_warm = flops / (us_warm * 1e-6) / 1e12
     achieved = flops / (split_us * 1e-6) / 1e12
-    traffic, mfma_busy = read_counters(args.workload, args.paged)
+    traffic, mfma_busy = read_counters(args.workload, args.paged) if H == 64 else (None, None)
     res = {
         "metric": "MLA verify attention us/call + TFLOP/s (% MFMA peak), H=64 q_len=9, prefix 16k",
         "value": round(tflops, 2),
@@ -270,10 +278,10 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tflops / (flops / (PAGES_US_Q9_P16384 * 1e-6) / 1e12), 2)
-        if args.workload == "q9_p16384" else None,
+        if args.workload == "q9_p16384" and H == 64 and not args.paged else None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": n, "heads": 64, "dl": 512,
+        "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": n, "heads": H, "dl": 512,
                    "dr": 64, "tree": case.meta["tree"], "scale": case.scale, "nsplit": plan.nsplit,
                    "chunk": plan.chunk, "pv_mode": args.pv_mode, "partials": "int16" if args.partials == 0 else "fp32",
                    "kv_layout": (f"paged, one token per page, pool {n + args.pool_extra} rows" if args.paged

@@ -60,12 +60,13 @@ extern "C" {
 #define MLAV_ERR_TREE 3        /* tree_parent is not topologically ordered (host check) */
 #define MLAV_ERR_ALIGN 4       /* a tensor pointer is not 16-byte aligned (lse and parents: 4) */
 #define MLAV_ERR_WORKSPACE 5   /* workspace missing or smaller than mla_verify_workspace_size */
-#define MLAV_ERR_UNSUPPORTED 6 /* a valid but unimplemented configuration (num_heads != 64) */
+#define MLAV_ERR_UNSUPPORTED 6 /* a valid but unimplemented configuration */
 #define MLAV_ERR_HIP 7         /* the HIP runtime reported an error */
 #define MLAV_ERR_ARG 8         /* a scalar or option value is invalid */
 
 #define MLAV_MAX_Q 64    /* q_len limit: one 64-bit ancestor mask per token */
-#define MLAV_HEADS 64    /* the head count the kernels are built for */
+#define MLAV_ROWS 64     /* (token, head) rows per workgroup: one row block */
+#define MLAV_MAX_HEADS 1024 /* num_heads limit */
 #define MLAV_DL 512      /* latent width (value width) */
 #define MLAV_DR 64       /* rope width */
 #define MLAV_MAX_KV 4000000 /* KV rows per sequence (byte offsets into one sequence's
@@ -117,7 +118,10 @@ typedef struct mlav_plan {
  *   scale           fp32 factor (> 0) on the whole 576-d dot product
  *   out             [q_len, num_heads, 512] fp32
  *   lse             [q_len, num_heads] fp32, natural log
- *   q_len           1 .. 64;  num_heads must be 64
+ *   q_len           1 .. 64;  num_heads 1 .. MLAV_MAX_HEADS (any count: a workgroup
+ *                   covers 64 consecutive (token, head) rows, so several tokens
+ *                   share one at num_heads < 64 and a token spans several at
+ *                   num_heads > 64)
  *   workspace       device scratch of at least mla_verify_workspace_size(...)
  *                   bytes (may be NULL when that size is 0)
  */
@@ -199,7 +203,10 @@ int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t
  *   part_out [plan->nsplit, q_len, num_heads, 512] fp32 and
  *   part_lse [plan->nsplit, q_len, num_heads] fp32 (natural log).
  * mla_verify_combine(part_out, part_lse, plan->nsplit, q_len * num_heads, ...)
- * then gives exactly what mla_verify returns. Partials from several callers
+ * then gives exactly what mla_verify returns (for q_len * num_heads not a
+ * multiple of 64 the rows are padded: part_out is [plan->nsplit, R, 512] with
+ * R = q_len * num_heads rounded up to a multiple of 64, and the combine then
+ * takes rows = R; the padding rows hold unspecified values). Partials from several callers
  * (e.g. KV shards) can be stacked and combined the same way; a split that sees
  * no visible key has lse = -inf and a zero output. The plan must satisfy
  * nsplit = ceil((prefix_len + q_len) / chunk) with chunk a positive multiple of

@@ -15,7 +15,7 @@ import torch
 
 from . import _lib
 
-H = 64
+H = 64  # the head count of the benchmark workloads (any count 1..1024 is accepted)
 DL = 512
 DR = 64
 
@@ -187,7 +187,9 @@ def mla_verify_partials(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: t
                         k_rope: torch.Tensor, tree_parent: torch.Tensor, prefix_len: int, scale: float,
                         plan: _lib.Plan, part_out: Optional[torch.Tensor] = None,
                         part_lse: Optional[torch.Tensor] = None, pv_mode: int = 0, kernel: int = 0):
-    """The split phase for `plan`: part_out [S, q, H, 512], part_lse [S, q, H] (fp32)."""
+    """The split phase for `plan`: part_out [S, q, H, 512], part_lse [S, q, H] (fp32); when
+    q * H is not a multiple of 64 the rows are padded: [S, R, 512] and [S, R] with R = q * H
+    rounded up to a multiple of 64."""
     dev = q_nope.device
     q, h = int(q_nope.shape[0]), int(q_nope.shape[1])
     n = int(prefix_len) + q
@@ -197,12 +199,15 @@ def mla_verify_partials(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: t
     _check(k_rope, "k_rope", torch.bfloat16, (n, DR), dev)
     _check(tree_parent, "tree_parent", torch.int32, (q,), dev)
     s = int(plan.nsplit)
+    # rows are (token, head) pairs in blocks of 64: padded when q * h is not a multiple of 64
+    rows = q * h
+    lead = (s, q, h) if rows % 64 == 0 else (s, (rows + 63) // 64 * 64)
     if part_out is None:
-        part_out = torch.empty(s, q, h, DL, dtype=torch.float32, device=dev)
+        part_out = torch.empty(lead + (DL,), dtype=torch.float32, device=dev)
     if part_lse is None:
-        part_lse = torch.empty(s, q, h, dtype=torch.float32, device=dev)
-    _check(part_out, "part_out", torch.float32, (s, q, h, DL), dev)
-    _check(part_lse, "part_lse", torch.float32, (s, q, h), dev)
+        part_lse = torch.empty(lead, dtype=torch.float32, device=dev)
+    _check(part_out, "part_out", torch.float32, lead + (DL,), dev)
+    _check(part_lse, "part_lse", torch.float32, lead, dev)
     opt = _lib.options(0, pv_mode, kernel)
     rc = _lib.load().mla_verify_partials(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(),
                                          k_rope.data_ptr(), tree_parent.data_ptr(), int(prefix_len),
@@ -235,7 +240,8 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor,
 
 
 def device_plan(q_len: int, batch: int, total_kv: int, max_kv: int, nsplit: int = 0, pv_mode: int = 0,
-                kernel: int = 0, device=None) -> _lib.Plan:
+                kernel: int = 0, device=None, num_heads: int = H) -> _lib.Plan:
     """The plan a call on `device` would use (reads the device's CU count)."""
     props = torch.cuda.get_device_properties(device if device is not None else torch.cuda.current_device())
-    return _lib.plan(q_len, H, batch, total_kv, max_kv, props.multi_processor_count, nsplit, pv_mode, kernel)
+    return _lib.plan(q_len, num_heads, batch, total_kv, max_kv, props.multi_processor_count, nsplit, pv_mode,
+                     kernel)

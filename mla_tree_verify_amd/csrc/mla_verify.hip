@@ -55,7 +55,7 @@
 
 namespace mlav {
 
-constexpr int kHeads = MLAV_HEADS;
+constexpr int kRows = MLAV_ROWS;  // (token, head) rows per workgroup
 constexpr int kDl = MLAV_DL;
 constexpr int kDr = MLAV_DR;
 constexpr int kTile = 32;                        // keys per wave tile
@@ -66,8 +66,8 @@ constexpr int kRing = 4;                         // tile slots: values, scores, 
 constexpr int kXchgBytes = 4 * 2 * 64 * 16;      // one exchange area: [4 waves][2 chunks][64 lanes][16 B]
 constexpr int kLdsBytes = kRing * kTileBytes + 2 * kXchgBytes;  // 163840 = all of a CU's LDS
 constexpr int kThreads = 256;
-static_assert(kRing * 128 == kDl && 128 * 4 * kHeads <= kTileBytes,
-              "the epilogue stages 128 output dims of all 64 heads in each ring slot");
+static_assert(kRing * 128 == kDl && 128 * 4 * kRows <= kTileBytes,
+              "the epilogue stages 128 output dims of all 64 rows in each ring slot");
 static_assert(kLdsBytes <= 163840, "LDS per workgroup");
 constexpr int kXcds = 8;
 constexpr int64_t kChunkGran = kTile;
@@ -104,6 +104,8 @@ struct Args {
   int64_t chunk;
   float scale_log2;
   int32_t q;
+  int32_t heads;         // query heads per token
+  int32_t nrb;           // row blocks per sequence: ceil(q * heads / 64)
   int32_t batch;
   int32_t nsplit;
   int32_t nwork;
@@ -146,6 +148,21 @@ __device__ inline uint64_t ancestor_mask_wave(int par_lane, int q, int t) {
   for (int step = 0; step < q && node >= 0 && node < q; ++step) {
     anc |= 1ull << node;
     node = __builtin_amdgcn_readlane(par_lane, node);
+  }
+  return anc;
+}
+
+// The same mask for a per-lane token t (rows of several tokens share a
+// wave): lane u holds parent[u] (u < q); each step fetches the parent of the
+// lane's current node from the lane that holds it. q steps for every lane.
+__device__ inline uint64_t ancestor_mask_lanes(int par_lane, int q, int t) {
+  uint64_t anc = 0;
+  int node = t;
+  for (int step = 0; step < q; ++step) {
+    const bool ok = node >= 0 && node < q;
+    anc |= ok ? 1ull << node : 0ull;
+    const int up = __shfl(par_lane, ok ? node : 0, 64);
+    node = ok ? up : -1;
   }
   return anc;
 }
@@ -252,25 +269,29 @@ __device__ inline int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Work id -> (sequence, split, token); tokens of one chunk are consecutive ids.
+// Work id -> (sequence, split, row block); the row blocks of one chunk are consecutive ids.
 // Values are made wave-uniform explicitly so that addresses built from them
 // stay in scalar registers.
 __device__ inline bool decode_work(const Args& a, int& b, int& s, int& t) {
   const int bid = blockIdx.x;
   const int w = uniform((bid % kXcds) * a.per_xcd + bid / kXcds);
   if (w >= a.nwork) return false;
-  t = uniform(w % a.q);
-  const int bs = uniform(w / a.q);
+  t = uniform(w % a.nrb);
+  const int bs = uniform(w / a.nrb);
   s = uniform(bs % a.nsplit);
   b = uniform(bs / a.nsplit);
   return true;
 }
 
-__device__ inline void write_nan_token(const Args& a, int b, int t, int tid, int nthreads) {
+// NaN into the output rows of row block rbk of sequence b (inconsistent offsets).
+__device__ inline void write_nan_rows(const Args& a, int b, int rbk, int tid, int nthreads) {
   const float nan = __builtin_nanf("");
-  float* o = a.out + ((int64_t)b * a.q + t) * kHeads * kDl;
-  for (int i = tid; i < kHeads * kDl; i += nthreads) o[i] = nan;
-  for (int i = tid; i < kHeads; i += nthreads) a.lse[((int64_t)b * a.q + t) * kHeads + i] = nan;
+  const int64_t rows_seq = (int64_t)a.q * a.heads;
+  const int64_t r0 = (int64_t)rbk * kRows;
+  const int nr = (int)(rows_seq - r0 < kRows ? rows_seq - r0 : kRows);
+  float* o = a.out + ((int64_t)b * rows_seq + r0) * kDl;
+  for (int i = tid; i < nr * kDl; i += nthreads) o[i] = nan;
+  for (int i = tid; i < nr; i += nthreads) a.lse[(int64_t)b * rows_seq + r0 + i] = nan;
 }
 
 // ---------------------------------------------------------------------------
@@ -425,7 +446,7 @@ __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&
 template <int kDh, bool kHiLo, bool kCompact, bool kPaged>
 __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r1, LDS_AS char* r2,
                                   LDS_AS char* r3, LDS_AS char* xs, LDS_AS char* xp, int b, int s,
-                                  int t, int wave, int hh, int lane, int64_t row0, int64_t n) {
+                                  int rbk, int wave, int hh, int lane, int64_t row0, int64_t n) {
   constexpr int kOwn = 8 * kDh;         // this wave's softmax elements
   constexpr int kSend = 8 * (1 - kDh);  // the partner's
   const int half = lane >> 5;
@@ -437,7 +458,14 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   const int c1 = c0 + chunk < n32 ? c0 + chunk : n32;
   const int nsplit_b = (n32 + chunk - 1) / chunk;
   const int ntiles = (c1 - c0 + kTile - 1) / kTile;
+  // This lane's row: row `head` of the block, (token, head) row r of the
+  // sequence, r = token * heads + head index; rows past q * heads pad the last
+  // block (they repeat the last row and are never stored).
   const int head = 32 * hh + (lane & 31);
+  const int rows_seq = a.q * a.heads;
+  const int r_lane = rbk * kRows + head;
+  const int r_src = r_lane < rows_seq ? r_lane : rows_seq - 1;
+  const int tok = r_src / a.heads;
 
   // Tile 0 is requested before anything else, then the queries and the
   // tree, then tiles 1 and 2, so that load latency overlaps the ancestor
@@ -504,7 +532,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   bf16x8_t qreg[18];
   first_tiles([&]() {
     par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
-    const int64_t qrow = ((int64_t)b * a.q + t) * kHeads + head;
+    const int64_t qrow = (int64_t)b * rows_seq + r_src;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
       const int d = 288 * kDh + 16 * ks + 8 * half;
@@ -529,7 +557,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     for (int m = 0; m < 4; ++m) vb[m] = kk * 1024 + 16 * (z0 ^ (4 * m)) + 8 * (i & 1);
   }
 
-  const uint64_t anc = ancestor_mask_wave(par_lane, a.q, t);
+  const uint64_t anc = ancestor_mask_lanes(par_lane, a.q, tok);
 
   const int partner = wave ^ 1;  // same head half, other dim half
   const KBases kb = make_kbases(lane & 31, half);
@@ -555,7 +583,13 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   float m_ref = -INFINITY;  // log2 units, this lane's head
   float l_run = 0.f;        // this lane's share of the softmax denominator (own keys)
   float m_seen = -INFINITY; // max over own keys
-  bool have_ref = false;    // uniform over the workgroup: a visible key has been seen
+  bool have_ref = false;    // this lane's row has seen a visible key (fixed its m_ref)
+  // A chunk that starts inside the prefix gives every row a visible key in
+  // its first tile, so all rows fix m_ref there. A chunk of tree keys only
+  // (rows of several tokens can see different keys) may leave rows without a
+  // reference after the first tile: its masked steps then exchange tile
+  // maxima so that each such row fixes m_ref at its first visible tile.
+  const bool ref_xchg = c0 >= prefix;  // uniform
   const float sl2 = a.scale_log2;  // > 0, so max(s) * sl2 = max(s * sl2)
   for (int attempt = 0; attempt < 2; ++attempt) {
 #pragma unroll
@@ -692,14 +726,14 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
         } else if (ks == 3) {
           const float mt = partner_max(smax) * sl2;  // max over this wave's 16 keys
           m_seen = fmax3(m_seen, mt);
-          if (kMasked && !have_ref && vis != 0) {
-            // first tile with a visible key: both halves' maxes fix m_ref
-            // (uniform over the workgroup: visibility is per token)
+          if (kMasked && ref_xchg) {
+            // a row's first tile with a visible key: both halves' maxes fix its m_ref
             __syncthreads();  // every wave has consumed its partner's scores
             *(LDS_AS float*)(xs + wave * 2048 + lane * 4) = mt;
             __syncthreads();
-            m_ref = fmax3(mt, *(const LDS_AS float*)(xs + partner * 2048 + lane * 4));
-            have_ref = true;
+            const bool adopt = !have_ref && vis != 0;
+            m_ref = adopt ? fmax3(mt, *(const LDS_AS float*)(xs + partner * 2048 + lane * 4)) : m_ref;
+            have_ref = have_ref || adopt;
           }
           ovf |= mt > m_ref + kRefHeadroom;
           mref = m_ref == -INFINITY ? 0.f : m_ref;
@@ -836,11 +870,12 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
 
   // Stage the accumulators through LDS so that each global store writes two
   // 512-byte row pieces instead of 32-byte pieces of 32 rows. Ring slot o
-  // takes dims [128 o, 128 o + 128) of all 64 heads (the slot of a write is
-  // then a compile-time choice); head h's 32 16-byte chunks sit at
-  // h * 512 + 16 * (c ^ (h & 15)), conflict-free for the head-per-lane writes
-  // and the chunk-per-lane reads. The reads apply 1 / l, kept per head in
-  // the weight-exchange area.
+  // takes dims [128 o, 128 o + 128) of all 64 rows (the slot of a write is
+  // then a compile-time choice); row h's 32 16-byte chunks sit at
+  // h * 512 + 16 * (c ^ (h & 15)), conflict-free for the row-per-lane writes
+  // and the chunk-per-lane reads. The reads apply 1 / l, kept per row in
+  // the weight-exchange area. Partials keep the padded row block (all 64
+  // rows); the final output takes the block's rows below q * heads only.
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_val = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   const bool final_write = nsplit_b == 1;
@@ -857,19 +892,20 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     }
   }
   __syncthreads();
-  const int64_t row_t = (int64_t)b * a.q + t;
-  const int64_t prow = (((int64_t)b * a.nsplit + s) * a.q + t) * kHeads;  // first partial row
+  const int64_t out_row0 = (int64_t)b * rows_seq + rbk * kRows;  // first output row of the block
+  const int nvalid = rows_seq - rbk * kRows < kRows ? rows_seq - rbk * kRows : kRows;
+  const int64_t prow = (((int64_t)b * a.nsplit + s) * a.nrb + rbk) * kRows;  // first partial row
   if (compact) {
-    // Compact partials: row h (one head) of the normalised partial is stored
+    // Compact partials: row h of the normalised partial is stored
     // as 512 int16 values q with one fp32 scale, value = q * scale, where
     // scale = (largest |value| of the row) / 32767; rounding to nearest keeps
     // every value within scale / 2, i.e. 2^-16 of the row's largest. Wave w
-    // handles heads [16 w, 16 w + 16) whole; lane l holds dims [8 l, 8 l + 8)
+    // handles rows [16 w, 16 w + 16) whole; lane l holds dims [8 l, 8 l + 8)
     // (ring slot l >> 4), so the row max is one wave reduction and each row
     // leaves as one contiguous 1 KB store.
     LDS_AS char* slot = ring(lane >> 4);
     const int cl = 2 * (lane & 15);
-    float my_scale = 0.f;  // lane k < 16 keeps the scale of head 16 w + k
+    float my_scale = 0.f;  // lane k < 16 keeps the scale of row 16 w + k
 #pragma unroll 4
     for (int k = 0; k < 16; ++k) {
       const int h = 16 * wave + k;
@@ -893,7 +929,8 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     }
     if (lane < 16) a.part_scale[prow + 16 * wave + lane] = my_scale;
   } else {
-    float* obase = final_write ? a.out + row_t * kHeads * kDl : a.part_o + prow * kDl;
+    float* obase = final_write ? a.out + out_row0 * kDl : a.part_o + prow * kDl;
+    const int nstore = final_write ? nvalid : kRows;
     // this wave stores ring slot `wave`: dims [128 wave, 128 wave + 128)
     LDS_AS char* slot = ring(wave);
     const int c = lane & 31;
@@ -902,13 +939,13 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       const int h = 2 * k + half;
       const f32x4_t v = *(const LDS_AS f32x4_t*)(slot + h * 512 + 16 * (c ^ (h & 15)));
       const float sc_h = *(const LDS_AS float*)(xp + h * 4);
-      *(f32x4_t*)(obase + (int64_t)h * kDl + 128 * wave + 4 * c) = v * sc_h;
+      if (h < nstore) *(f32x4_t*)(obase + (int64_t)h * kDl + 128 * wave + 4 * c) = v * sc_h;
     }
   }
   if (kDh == 0 && half == 0) {
-    if (final_write)
-      a.lse[row_t * kHeads + head] = lse_val;
-    else
+    if (final_write) {
+      if (head < nvalid) a.lse[out_row0 + head] = lse_val;
+    } else
       a.part_lse[prow + head] = lse_val;
   }
 }
@@ -932,15 +969,15 @@ void split_mfma_kernel(Args a) {
   // loads (fetched lazily, each group would wait on its own round trip).
   asm volatile("" ::"s"(a.qn), "s"(a.qr), "s"(a.lat), "s"(a.rope), "s"(a.parent), "s"(a.offs),
                "s"(a.single_n), "s"(a.total_kv), "s"(a.max_kv), "s"(a.chunk), "s"(a.scale_log2), "s"(a.q),
-               "s"(a.nsplit), "s"(a.nwork), "s"(a.per_xcd));
-  int b, s, t;
+               "s"(a.heads), "s"(a.nrb), "s"(a.nsplit), "s"(a.nwork), "s"(a.per_xcd));
+  int b, s, t;  // t: the row block
   if (!decode_work(a, b, s, t)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   int64_t row0, n;
   if (!seq_bounds(a, b, row0, n)) {
-    if (s == 0) write_nan_token(a, b, t, tid, kThreads);
+    if (s == 0) write_nan_rows(a, b, t, tid, kThreads);
     return;
   }
   row0 = uniform64(row0);
@@ -960,25 +997,29 @@ void split_mfma_kernel(Args a) {
 __device__ inline float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 __global__ __launch_bounds__(kThreads) void split_valu_kernel(Args a) {
-  const int work = blockIdx.x >> 4;  // 16 workgroups x 4 waves = 64 heads per work item
-  const int head = ((blockIdx.x & 15) << 2) + (threadIdx.x >> 6);
+  const int work = blockIdx.x >> 4;  // 16 workgroups x 4 waves = the 64 rows of a row block
+  const int head = ((blockIdx.x & 15) << 2) + (threadIdx.x >> 6);  // row in the block
   const int lane = threadIdx.x & 63;
   if (work >= a.nwork) return;
-  const int t = work % a.q;
-  const int s = (work / a.q) % a.nsplit;
-  const int b = work / (a.q * a.nsplit);
+  const int rbk = work % a.nrb;
+  const int s = (work / a.nrb) % a.nsplit;
+  const int b = work / (a.nrb * a.nsplit);
   int64_t row0, n;
   if (!seq_bounds(a, b, row0, n)) {
-    if (s == 0 && (blockIdx.x & 15) == 0) write_nan_token(a, b, t, threadIdx.x, kThreads);
+    if (s == 0 && (blockIdx.x & 15) == 0) write_nan_rows(a, b, rbk, threadIdx.x, kThreads);
     return;
   }
+  const int rows_seq = a.q * a.heads;
+  const int r = rbk * kRows + head;  // (token, head) row of the sequence
+  if (r >= rows_seq) return;
+  const int t = r / a.heads;
   const int64_t prefix = n - a.q;
   const int64_t c0 = (int64_t)s * a.chunk;
   if (c0 >= n) return;
   const int64_t c1 = c0 + a.chunk < n ? c0 + a.chunk : n;
   const int nsplit_b = (int)((n + a.chunk - 1) / a.chunk);
   const uint64_t anc = ancestor_mask(a.parent + (int64_t)b * a.q, a.q, t);
-  const int64_t qrow = ((int64_t)b * a.q + t) * kHeads + head;
+  const int64_t qrow = (int64_t)b * rows_seq + r;
 
   // lane owns query dims [8 lane, 8 lane + 8) of the latent part and dim `lane` of the rope part
   float qv[9];
@@ -1016,15 +1057,14 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(Args a) {
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const float lse_val = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
   const bool final_write = nsplit_b == 1;
-  float* orow = final_write
-                    ? a.out + qrow * kDl
-                    : a.part_o + ((((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head) * kDl;
+  const int64_t prow = (((int64_t)b * a.nsplit + s) * a.nrb + rbk) * kRows + head;  // padded partial row
+  float* orow = final_write ? a.out + qrow * kDl : a.part_o + prow * kDl;
   for (int d = 0; d < 8; ++d) orow[8 * lane + d] = acc[d] * inv;
   if (lane == 0) {
     if (final_write)
       a.lse[qrow] = lse_val;
     else
-      a.part_lse[(((int64_t)b * a.nsplit + s) * a.q + t) * kHeads + head] = lse_val;
+      a.part_lse[prow] = lse_val;
   }
 }
 
@@ -1035,7 +1075,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
   if (row >= rows) return;
   const int d4 = threadIdx.x & 127;
-  const int64_t rows_b = (int64_t)a.q * kHeads;
+  const int64_t rows_b = (int64_t)a.q * a.heads;      // output rows per sequence
+  const int64_t rows_pad = (int64_t)a.nrb * kRows;     // partial rows per (sequence, split)
   const int b = (int)(row / rows_b);
   const int64_t rb = row - (int64_t)b * rows_b;
   int ns = a.fixed_ns;
@@ -1050,8 +1091,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
     ns = (int)((n + a.chunk - 1) / a.chunk);
     if (ns <= 1) return;  // the split kernel wrote this row directly
   }
-  const float* pl = a.part_lse + (int64_t)b * a.nsplit * rows_b + rb;
-  const float* po = a.part_o + ((int64_t)b * a.nsplit * rows_b + rb) * kDl + 4 * d4;
+  const float* pl = a.part_lse + (int64_t)b * a.nsplit * rows_pad + rb;
+  const float* po = a.part_o + ((int64_t)b * a.nsplit * rows_pad + rb) * kDl + 4 * d4;
   // Batches of up to 32 splits: every lse and partial load of a batch is
   // issued before any is used (one memory round trip per batch); batches are
   // merged with a running max. Entries past the last split reload the last
@@ -1067,8 +1108,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int sk = s0 + k < ns ? s0 + k : ns - 1;
-      lz[k] = pl[(int64_t)sk * rows_b];
-      o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_b * kDl));
+      lz[k] = pl[(int64_t)sk * rows_pad];
+      o[k] = __builtin_nontemporal_load((const f32x4_t*)(po + (int64_t)sk * rows_pad * kDl));
     }
     float mb = -INFINITY;
 #pragma unroll
@@ -1091,18 +1132,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   if (d4 == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
 
-// Combine of compact (int16 + scale) partials: one wave per row; lane l owns
-// dims [8 l, 8 l + 8), one 16-byte load per split. Splits go in batches of 32
-// (one memory round trip for up to 32 splits): every partial load of a batch
-// is issued first, lanes 0..31 fetch the batch's lse and scale values, the
-// batch max and weight sum come from 32-lane reductions, and each split's
-// weight * scale reaches all lanes by readlane.
-// Batches are merged with a running max, as in the fp32 combine.
+// Combine of compact (int16 + scale) partials, up to 32 splits: one wave per
+// row; lane l owns dims [8 l, 8 l + 8), one 16-byte load per split, and all
+// loads of a row are in flight together (one memory round trip). Lanes 0..31
+// fetch the lse and scale values, the max and weight sum come from 32-lane
+// reductions, and each split's weight * scale reaches all lanes by readlane.
 __global__ __launch_bounds__(kThreads) void combine_compact_kernel(Args a, int64_t rows) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
-  const int64_t rows_b = (int64_t)a.q * kHeads;
+  const int64_t rows_b = (int64_t)a.q * a.heads;   // output rows per sequence
+  const int64_t rows_pad = (int64_t)a.nrb * kRows;  // partial rows per (sequence, split)
   const int b = (int)(row / rows_b);
   const int64_t rb = row - (int64_t)b * rows_b;
   int64_t row0, n;
@@ -1115,24 +1155,94 @@ __global__ __launch_bounds__(kThreads) void combine_compact_kernel(Args a, int64
   }
   const int ns = (int)((n + a.chunk - 1) / a.chunk);
   if (ns <= 1) return;  // the split kernel wrote this row directly
-  const int64_t base = (int64_t)b * a.nsplit * rows_b + rb;  // partial row of split 0
+  const int64_t base = (int64_t)b * a.nsplit * rows_pad + rb;  // partial row of split 0
   const float* pl = a.part_lse + base;
   const float* psc = a.part_scale + base;
   const int16_t* pq = a.part_q + base * kDl + 8 * lane;
   constexpr int kBatch = 32;
+  u32x4_t qv[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int sk = k < ns ? k : ns - 1;  // past the end: reload the last (weight 0)
+    qv[k] = __builtin_nontemporal_load((const u32x4_t*)(pq + (int64_t)sk * rows_pad * kDl));
+  }
+  const bool mine = lane < ns;
+  const float lz = mine ? pl[(int64_t)lane * rows_pad] : -INFINITY;
+  const float sc = mine ? psc[(int64_t)lane * rows_pad] : 0.f;
+  const float M = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_max(lz))));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    const float w = mine ? __builtin_amdgcn_exp2f((lz - M) * kLog2e) : 0.f;
+    wsum = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_sum(w))));
+    const float f = w * sc;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), k));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int32_t v = (int32_t)qv[k][e];
+        acc[2 * e] += fk * (float)((v << 16) >> 16);
+        acc[2 * e + 1] += fk * (float)(v >> 16);
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv;
+  *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv;
+  if (lane == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+}
+
+// Combine of compact (int16 + scale) partials for more than 32 splits: one
+// workgroup per row; wave w merges splits [w ns / 4, (w + 1) ns / 4) and the
+// four partial merges meet in LDS. Lane l owns dims [8 l, 8 l + 8), one 16-byte load per split. A
+// wave takes its splits in batches of 32 (one memory round trip each): every
+// partial load of a batch is issued first, lanes 0..31 fetch the batch's lse
+// and scale values, the batch max and weight sum come from 32-lane
+// reductions, each split's weight * scale reaches all lanes by readlane, and
+// batches are merged with a running max, as in the fp32 combine.
+__global__ __launch_bounds__(kThreads) void combine_compact_wide_kernel(Args a, int64_t rows) {
+  __shared__ float x_acc[4][kDl];
+  __shared__ float x_m[4], x_w[4];
+  const int64_t row = blockIdx.x;
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int64_t rows_b = (int64_t)a.q * a.heads;   // output rows per sequence
+  const int64_t rows_pad = (int64_t)a.nrb * kRows;  // partial rows per (sequence, split)
+  const int b = (int)(row / rows_b);
+  const int64_t rb = row - (int64_t)b * rows_b;
+  int64_t row0, n;
+  if (!seq_bounds(a, b, row0, n)) {
+    if (wave == 0) {
+      const float nan = __builtin_nanf("");
+      *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){nan, nan, nan, nan};
+      *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){nan, nan, nan, nan};
+      if (lane == 0) a.lse[row] = nan;
+    }
+    return;
+  }
+  const int ns = (int)((n + a.chunk - 1) / a.chunk);
+  if (ns <= 1) return;  // the split kernel wrote this row directly
+  const int64_t base = (int64_t)b * a.nsplit * rows_pad + rb;  // partial row of split 0
+  const float* pl = a.part_lse + base;
+  const float* psc = a.part_scale + base;
+  const int16_t* pq = a.part_q + base * kDl + 8 * lane;
+  const int s_lo = wave * ns / 4, s_hi = (wave + 1) * ns / 4;
+  constexpr int kBatch = 32;
   float M = -INFINITY, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += kBatch) {
+  for (int s0 = s_lo; s0 < s_hi; s0 += kBatch) {
     u32x4_t qv[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int sk = s0 + k < ns ? s0 + k : ns - 1;  // past the end: reload the last (weight 0)
-      qv[k] = __builtin_nontemporal_load((const u32x4_t*)(pq + (int64_t)sk * rows_b * kDl));
+      const int sk = s0 + k < s_hi ? s0 + k : s_hi - 1;  // past the end: reload the last (weight 0)
+      qv[k] = __builtin_nontemporal_load((const u32x4_t*)(pq + (int64_t)sk * rows_pad * kDl));
     }
     const int sl = s0 + (lane & 31);
-    const bool mine = lane < kBatch && sl < ns;
-    const float lz = mine ? pl[(int64_t)sl * rows_b] : -INFINITY;
-    const float sc = mine ? psc[(int64_t)sl * rows_b] : 0.f;
+    const bool mine = lane < kBatch && sl < s_hi;
+    const float lz = mine ? pl[(int64_t)sl * rows_pad] : -INFINITY;
+    const float sc = mine ? psc[(int64_t)sl * rows_pad] : 0.f;
     const float bmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_max(lz))));
     if (bmax == -INFINITY) continue;  // every split of this batch is empty (uniform)
     const float m_new = fmax3(M, bmax);
@@ -1155,10 +1265,33 @@ __global__ __launch_bounds__(kThreads) void combine_compact_kernel(Args a, int64
       }
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv;
-  *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv;
-  if (lane == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+  // merge the four waves' (M, wsum, acc) in LDS
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x_acc[wave][8 * lane + e] = acc[e];
+  if (lane == 0) {
+    x_m[wave] = M;
+    x_w[wave] = wsum;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float mm = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) mm = fmax3(mm, x_m[w]);
+  float tot = 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (mm != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float r = __builtin_amdgcn_exp2f((x_m[w] - mm) * kLog2e);  // 0 for a wave with nothing
+      tot += r * x_w[w];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += r * x_acc[w][8 * lane + e];
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){o[0], o[1], o[2], o[3]} * inv;
+  *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){o[4], o[5], o[6], o[7]} * inv;
+  if (lane == 0) a.lse[row] = tot > 0.f ? mm + __builtin_amdgcn_logf(tot) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1191,23 +1324,25 @@ int check_options(const mlav_options* opt) {
   return MLAV_OK;
 }
 
+// Row blocks of one sequence: its q * heads (token, head) rows in blocks of 64.
+int32_t row_blocks(int32_t q, int32_t heads) { return (q * heads + kRows - 1) / kRows; }
+
 int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t max_kv,
               int32_t num_cus, const mlav_options* opt, mlav_plan* p) {
-  if (q < 1 || q > MLAV_MAX_Q || batch < 1 || heads < 1) return MLAV_ERR_SHAPE;
-  if (heads != kHeads) return MLAV_ERR_UNSUPPORTED;
+  if (q < 1 || q > MLAV_MAX_Q || batch < 1 || heads < 1 || heads > MLAV_MAX_HEADS) return MLAV_ERR_SHAPE;
   if (max_kv < q || total_kv < (int64_t)batch * q || max_kv > total_kv) return MLAV_ERR_SHAPE;
   if (max_kv > MLAV_MAX_KV) return MLAV_ERR_SHAPE;
   if (num_cus < 1) return MLAV_ERR_ARG;
   const int rc = check_options(opt);
   if (rc != MLAV_OK) return rc;
-  const int64_t tokens = (int64_t)batch * q;
+  const int64_t blocks = (int64_t)batch * row_blocks(q, heads);  // row blocks of the whole call
   int64_t chunk;
   if (opt && opt->nsplit > 0) {
     chunk = (max_kv + opt->nsplit - 1) / opt->nsplit;
     chunk = (chunk + kChunkGran - 1) / kChunkGran * kChunkGran;
   } else {
     // one resident workgroup per CU: aim for about num_cus workgroups in total
-    int64_t s_avg = num_cus / tokens;
+    int64_t s_avg = num_cus / blocks;
     if (s_avg < 1) s_avg = 1;
     const int64_t avg_kv = (total_kv + batch - 1) / batch;
     chunk = (avg_kv + s_avg - 1) / s_avg;
@@ -1215,7 +1350,7 @@ int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t
     if (chunk < kMinChunk) chunk = kMinChunk;
   }
   const int64_t ns = (max_kv + chunk - 1) / chunk;
-  const int64_t nwork = tokens * ns;
+  const int64_t nwork = blocks * ns;
   if (nwork > (int64_t(1) << 30)) return MLAV_ERR_SHAPE;
   p->nsplit = (int32_t)ns;
   p->tile = kTile;
@@ -1232,21 +1367,23 @@ int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t
 }
 
 // Split partials in the workspace: values, then lse, then (compact only) the
-// per-row scales. Compact values are int16: [B, S, q, H, 512] x 2 bytes.
+// per-row scales, over [B, S, nrb * 64] rows (each sequence's q * heads rows
+// padded to whole row blocks). Compact values are int16: 1024 bytes per row.
 bool compact_partials(const mlav_options* opt) {
   // the VALU cross-check kernel writes fp32 partials only
   return (opt ? opt->partials : 0) == 0 && (opt ? opt->kernel : 0) == 0;
 }
 
-size_t workspace_bytes_for(const mlav_plan& p, int32_t q, int32_t batch, bool compact) {
+size_t workspace_bytes_for(const mlav_plan& p, int32_t q, int32_t heads, int32_t batch, bool compact) {
   if (!p.combine) return 0;
-  const size_t rows = (size_t)batch * p.nsplit * q * kHeads;
+  const size_t rows = (size_t)batch * p.nsplit * row_blocks(q, heads) * kRows;
   return compact ? rows * (kDl * sizeof(int16_t) + 2 * sizeof(float)) : rows * (kDl + 1) * sizeof(float);
 }
 
 // Points the partial pointers of `a` into the workspace (layout above).
-void set_partials(Args& a, void* workspace, const mlav_plan& p, int32_t q, int32_t batch, bool compact) {
-  const size_t rows = (size_t)batch * p.nsplit * q * kHeads;
+void set_partials(Args& a, void* workspace, const mlav_plan& p, int32_t q, int32_t heads, int32_t batch,
+                  bool compact) {
+  const size_t rows = (size_t)batch * p.nsplit * row_blocks(q, heads) * kRows;
   a.part_o = nullptr;
   a.part_q = nullptr;
   a.part_scale = nullptr;
@@ -1269,7 +1406,8 @@ int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* 
   Args a = base;
   a.nsplit = p.nsplit;
   a.chunk = p.chunk;
-  a.nwork = a.batch * a.q * p.nsplit;
+  a.nrb = row_blocks(a.q, a.heads);
+  a.nwork = a.batch * a.nrb * p.nsplit;
   a.per_xcd = (a.nwork + kXcds - 1) / kXcds;
   a.fixed_ns = 0;
   const int kernel = opt ? opt->kernel : 0;
@@ -1294,11 +1432,15 @@ int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* 
   if (phase == 1) return MLAV_OK;
 merge:
   if (p.combine) {
-    const int64_t rows = (int64_t)a.batch * a.q * kHeads;
-    if (compact)
-      hipLaunchKernelGGL(combine_compact_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, a, rows);
-    else
+    const int64_t rows = (int64_t)a.batch * a.q * a.heads;
+    if (compact) {
+      if (p.nsplit <= 32)
+        hipLaunchKernelGGL(combine_compact_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, a, rows);
+      else
+        hipLaunchKernelGGL(combine_compact_wide_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, rows);
+    } else {
       hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
+    }
     if (hipGetLastError() != hipSuccess) return MLAV_ERR_HIP;
   }
   return MLAV_OK;
@@ -1308,8 +1450,7 @@ int common_checks(const void* qn, const void* qr, const void* lat, const void* r
                   const int32_t* parent, float scale, const float* out, const float* lse,
                   int32_t q, int32_t heads, const mlav_options* opt) {
   if (!qn || !qr || !lat || !rope || !parent || !out || !lse) return MLAV_ERR_NULL;
-  if (q < 1 || q > MLAV_MAX_Q || heads < 1) return MLAV_ERR_SHAPE;
-  if (heads != kHeads) return MLAV_ERR_UNSUPPORTED;
+  if (q < 1 || q > MLAV_MAX_Q || heads < 1 || heads > MLAV_MAX_HEADS) return MLAV_ERR_SHAPE;
   if (!aligned(qn, 16) || !aligned(qr, 16) || !aligned(lat, 16) || !aligned(rope, 16) ||
       !aligned(out, 16) || !aligned(lse, 4) || !aligned(parent, 4))
     return MLAV_ERR_ALIGN;
@@ -1335,7 +1476,7 @@ size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch
   if (num_cus <= 0 && device_cus(&num_cus) != MLAV_OK) return 0;
   mlav_plan p;
   if (plan_impl(q_len, num_heads, batch, total_kv, max_kv, num_cus, opt, &p) != MLAV_OK) return 0;
-  return workspace_bytes_for(p, q_len, batch, compact_partials(opt));
+  return workspace_bytes_for(p, q_len, num_heads, batch, compact_partials(opt));
 }
 
 int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
@@ -1355,7 +1496,7 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
   rc = plan_impl(q_len, num_heads, 1, n, n, cus, opt, &p);
   if (rc != MLAV_OK) return rc;
   const bool compact = compact_partials(opt);
-  const size_t need = workspace_bytes_for(p, q_len, 1, compact);
+  const size_t need = workspace_bytes_for(p, q_len, num_heads, 1, compact);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
   Args a{};
@@ -1367,12 +1508,13 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
   a.offs = nullptr;
   a.out = out;
   a.lse = lse;
-  set_partials(a, workspace, p, q_len, 1, compact);
+  set_partials(a, workspace, p, q_len, num_heads, 1, compact);
   a.single_n = n;
   a.total_kv = n;
   a.max_kv = n;
   a.scale_log2 = scale * kLog2e;
   a.q = q_len;
+  a.heads = num_heads;
   a.batch = 1;
   return launch(a, p, opt, stream);
 }
@@ -1405,7 +1547,7 @@ int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, cons
   rc = plan_impl(q_len, num_heads, batch, total_kv, max_kv, cus, opt, &p);
   if (rc != MLAV_OK) return rc;
   const bool compact = compact_partials(opt);
-  const size_t need = workspace_bytes_for(p, q_len, batch, compact);
+  const size_t need = workspace_bytes_for(p, q_len, num_heads, batch, compact);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
   Args a{};
@@ -1417,12 +1559,13 @@ int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, cons
   a.offs = kv_offsets;
   a.out = out;
   a.lse = lse;
-  set_partials(a, workspace, p, q_len, batch, compact);
+  set_partials(a, workspace, p, q_len, num_heads, batch, compact);
   a.single_n = 0;
   a.total_kv = total_kv;
   a.max_kv = max_kv;
   a.scale_log2 = scale * kLog2e;
   a.q = q_len;
+  a.heads = num_heads;
   a.batch = batch;
   return launch(a, p, opt, stream);
 }
@@ -1453,7 +1596,7 @@ int32_t mla_verify_paged(const void* q_nope_absorbed, const void* q_rope, const 
   rc = plan_impl(q_len, num_heads, batch, total_kv, max_kv, cus, opt, &p);
   if (rc != MLAV_OK) return rc;
   const bool compact = compact_partials(opt);
-  const size_t need = workspace_bytes_for(p, q_len, batch, compact);
+  const size_t need = workspace_bytes_for(p, q_len, num_heads, batch, compact);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
   Args a{};
@@ -1467,12 +1610,13 @@ int32_t mla_verify_paged(const void* q_nope_absorbed, const void* q_rope, const 
   a.pool_rows = pool_rows;
   a.out = out;
   a.lse = lse;
-  set_partials(a, workspace, p, q_len, batch, compact);
+  set_partials(a, workspace, p, q_len, num_heads, batch, compact);
   a.single_n = kv_offsets ? 0 : total_kv;
   a.total_kv = total_kv;
   a.max_kv = max_kv;
   a.scale_log2 = scale * kLog2e;
   a.q = q_len;
+  a.heads = num_heads;
   a.batch = batch;
   return launch(a, p, opt, stream);
 }
@@ -1493,7 +1637,7 @@ int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, con
     return MLAV_ERR_ARG;
   mlav_plan p = *plan;
   const int kernel = opt ? opt->kernel : 0;
-  const int64_t nwork = (int64_t)q_len * p.nsplit;
+  const int64_t nwork = (int64_t)row_blocks(q_len, num_heads) * p.nsplit;
   p.grid = kernel == 0 ? (int32_t)((nwork + kXcds - 1) / kXcds * kXcds) : (int32_t)(nwork * 16);
   p.combine = 0;
   Args a{};
@@ -1513,6 +1657,7 @@ int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, con
   a.max_kv = n;
   a.scale_log2 = scale * kLog2e;
   a.q = q_len;
+  a.heads = num_heads;
   a.batch = 1;
   return launch(a, p, opt, stream);
 }
@@ -1531,13 +1676,15 @@ int32_t mla_verify_combine(const float* part_out, const float* part_lse, int32_t
   if (nsplit < 1 || rows < 1 || rows > (int64_t(1) << 34)) return MLAV_ERR_SHAPE;
   if (!aligned(part_out, 16) || !aligned(out, 16) || !aligned(part_lse, 4) || !aligned(lse, 4))
     return MLAV_ERR_ALIGN;
-  if (rows % kHeads != 0) return MLAV_ERR_SHAPE;  // rows are (token, head) pairs
+  if (rows % kRows != 0) return MLAV_ERR_SHAPE;  // whole row blocks (padded partial layout)
   Args a{};
   a.part_o = const_cast<float*>(part_out);
   a.part_lse = const_cast<float*>(part_lse);
   a.out = out;
   a.lse = lse;
-  a.q = (int32_t)(rows / kHeads);
+  a.q = (int32_t)(rows / kRows);  // one block of 64 rows per "token"
+  a.heads = kRows;
+  a.nrb = a.q;
   a.batch = 1;
   a.nsplit = nsplit;
   a.fixed_ns = nsplit;
@@ -1555,7 +1702,7 @@ const char* mla_verify_strerror(int32_t status) {
     case MLAV_ERR_TREE: return "tree_parent is not topologically ordered";
     case MLAV_ERR_ALIGN: return "a pointer is not aligned (16 B for tensors, 4 B for lse/parents)";
     case MLAV_ERR_WORKSPACE: return "workspace missing or too small";
-    case MLAV_ERR_UNSUPPORTED: return "unsupported configuration (num_heads must be 64)";
+    case MLAV_ERR_UNSUPPORTED: return "unsupported configuration";
     case MLAV_ERR_HIP: return "HIP runtime error";
     case MLAV_ERR_ARG: return "invalid scalar or option value";
     default: return "unknown status";

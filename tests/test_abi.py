@@ -86,14 +86,17 @@ def test_workspace_size(lib):
     # the VALU cross-check kernel always uses fp32 partials
     assert _lib.workspace_size(9, 64, 1, n, n, num_cus=256, kernel=1) == pl.nsplit * 9 * 64 * 513 * 4
     assert _lib.workspace_size(9, 64, 1, 265, 265, num_cus=256, nsplit=1) == 0
-    assert _lib.workspace_size(9, 32, 1, n, n, num_cus=256) == 0  # unsupported -> 0
+    # any head count: 9 x 8 = 72 rows -> 2 row blocks of 64
+    pl8 = _lib.plan(9, 8, 1, n, n, 256)
+    assert _lib.workspace_size(9, 8, 1, n, n, num_cus=256) == pl8.nsplit * 2 * 64 * (512 * 2 + 8)
+    assert _lib.workspace_size(9, 1025, 1, n, n, num_cus=256) == 0  # beyond MLAV_MAX_HEADS -> 0
     assert _lib.workspace_size(0, 64, 1, n, n, num_cus=256) == 0
 
 
 def test_plan_errors(lib):
     with pytest.raises(_lib.MLAVError) as e:
-        _lib.plan(9, 32, 1, 100, 100, 256)
-    assert e.value.status == _lib.MLAV_ERR_UNSUPPORTED
+        _lib.plan(9, 1025, 1, 100, 100, 256)
+    assert e.value.status == _lib.MLAV_ERR_SHAPE
     for args in [(0, 64, 1, 100, 100, 256), (65, 64, 1, 100, 100, 256), (9, 64, 1, 5, 5, 256),
                  (9, 64, 2, 100, 200, 256)]:
         with pytest.raises(_lib.MLAVError) as e:
@@ -126,8 +129,7 @@ def test_host_validation_errors(lib):
     assert call(lib, q=0) == _lib.MLAV_ERR_SHAPE
     assert call(lib, q=65) == _lib.MLAV_ERR_SHAPE
     assert call(lib, h=0) == _lib.MLAV_ERR_SHAPE
-    assert call(lib, h=16) == _lib.MLAV_ERR_UNSUPPORTED
-    assert call(lib, h=128) == _lib.MLAV_ERR_UNSUPPORTED
+    assert call(lib, h=1025) == _lib.MLAV_ERR_SHAPE
     assert call(lib, prefix=-1) == _lib.MLAV_ERR_SHAPE
     for k in ("qn", "qr", "lat", "rope", "out"):
         assert call(lib, **{k: A + 8}) == _lib.MLAV_ERR_ALIGN
@@ -191,3 +193,14 @@ def test_paged_validation_errors(lib):
     assert c(batch=2, total=600, maxkv=300) == _lib.MLAV_ERR_ARG
     assert c(maxkv=200) == _lib.MLAV_ERR_ARG
     assert c(offs=A + 4, batch=2, total=600, maxkv=300) == _lib.MLAV_ERR_ALIGN
+
+
+def test_plan_counts_row_blocks(lib):
+    """The planner fills the CUs with (row block, split) work items: a row
+    block is 64 consecutive (token, head) rows, so H = 8 at q = 9 has 2 blocks
+    and H = 128 has 18."""
+    n = 16393
+    for heads, blocks in ((64, 9), (8, 2), (16, 3), (128, 18), (1, 1)):
+        pl = _lib.plan(9, heads, 1, n, n, 256)
+        assert pl.grid >= blocks * pl.nsplit and pl.grid % 8 == 0
+        assert blocks * pl.nsplit <= 256 or pl.chunk == 128

@@ -298,3 +298,67 @@ def test_compact_partials_within_bound(name):
     ro, rl = oracle(case) if name != "q9_p65536_chain" else (None, None)
     if ro is not None:
         assert_parity(oc, lc, ro, rl, f"{name} compact partials")
+
+
+# ---------------------------------------------------------------------------
+# head counts other than 64: a workgroup covers 64 consecutive (token, head)
+# rows, so rows of several tokens (different tree masks) share a workgroup
+# below 64 heads and a token spans several workgroups above
+# ---------------------------------------------------------------------------
+HEADS_CASES = [
+    (8, 9, 4096, "random", 0), (8, 9, 300, "random", 0), (16, 9, 1000, "random", 0), (16, 33, 2048, "bounded", 0),
+    (32, 9, 777, "chain", 0), (128, 9, 2000, "random", 0), (128, 33, 500, "bounded", 0), (1, 9, 300, "random", 0),
+    (48, 5, 900, "random", 0), (8, 64, 1000, "random", 0),
+    # chunks made of tree keys only: rows fix their reference max at their own first visible tile
+    (8, 40, 0, "random", 0), (16, 40, 64, "random", 2), (64, 40, 64, "random", 2), (8, 64, 32, "chain", 3),
+]
+
+
+@pytest.mark.parametrize("heads,q,p,tree,nsplit", HEADS_CASES)
+def test_head_counts(heads, q, p, tree, nsplit):
+    case = gen.make_case(q, p, tree=tree, num_heads=heads, seed=4000 + heads + q + p)
+    out, lse = run(case, nsplit=nsplit)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, f"H={heads} q={q} p={p}")
+
+
+@pytest.mark.parametrize("heads", [8, 128])
+def test_head_counts_valu_kernel(heads):
+    case = gen.make_case(9, 700, tree="random", num_heads=heads, seed=4100 + heads)
+    out, lse = run(case, kernel=1)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, f"valu H={heads}")
+
+
+def test_head_counts_batched():
+    case = gen.make_batched_case(3, 9, prefix_lens=[100, 1500, 40], tree="random", num_heads=16, seed=4200)
+    out, lse = run(case)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, "batched H=16")
+
+
+def test_head_counts_partials_padded_rows():
+    """q * H = 72 rows: partials come in two padded blocks of 64 rows and the
+    combine of the first 72 equals the full call."""
+    case = gen.make_case(9, 3000, tree="random", num_heads=8, seed=4300)
+    d = dev_case(case)
+    out, lse = run(case, partials=1)
+    pl = api.device_plan(9, 1, 3009, 3009, num_heads=8)
+    assert pl.nsplit > 1
+    po, pls = api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
+                                      3000, case.scale, pl)
+    assert tuple(po.shape) == (pl.nsplit, 128, 512)
+    o2, l2 = api.combine(po, pls)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu()[:72].view_as(out), out) and torch.equal(l2.cpu()[:72].view_as(lse), lse)
+
+
+@pytest.mark.parametrize("nsplit", [5, 32, 33, 40, 100])
+def test_compact_combine_split_counts(nsplit):
+    """Both combine forms of the int16 partials (one wave per row up to 32
+    splits, four waves per row beyond) against the oracle."""
+    case = gen.make_case(9, 6000, tree="random", seed=4400 + nsplit)
+    pl = api.device_plan(9, 1, 6009, 6009, nsplit=nsplit)
+    out, lse = run(case, nsplit=nsplit)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, f"compact, {pl.nsplit} splits")
