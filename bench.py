@@ -51,6 +51,8 @@ def parse():
                     help="read the KV through a page table (one token per page): the rows scattered over a pool "
                          "by a seeded random permutation, through mla_verify_paged")
     ap.add_argument("--pool-extra", type=int, default=0, help="paged: pool rows beyond the workload's KV rows")
+    ap.add_argument("--nsplit", type=int, default=0, help="force the KV split count (0: the planner's)")
+    ap.add_argument("--prefix", type=int, default=-1, help="override the workload's prefix length")
     ap.add_argument("--heads", type=int, default=64,
                     help="query heads per token (the workload's shape with this head count; 64 is the metric's)")
     return ap.parse_args()
@@ -124,20 +126,22 @@ def main() -> int:
     if spec["kind"] != "single":
         print(json.dumps({"error": "bench.py times single-sequence workloads"}))
         return 2
-    if args.heads == 64:
+    if args.heads == 64 and args.prefix < 0:
         case = gen.make_workload(args.workload)
     else:
         kw = dict(gen.WORKLOADS[args.workload])
         kw.pop("kind")
+        if args.prefix >= 0:
+            kw["prefix_len"] = args.prefix
         case = gen.make_case(num_heads=args.heads, **kw)
     q, p = case.q_len, case.prefix_len
     n = p + q
     H = args.heads
     flops = orc.algorithmic_flops(case.tree_parent, p, num_heads=H)
     alg_bytes = orc.algorithmic_bytes(q, n, num_heads=H)
-    plan = api.device_plan(q, 1, n, n, pv_mode=args.pv_mode, num_heads=H)
+    plan = api.device_plan(q, 1, n, n, nsplit=args.nsplit, pv_mode=args.pv_mode, num_heads=H)
     lib = _lib.load()
-    ws_bytes = _lib.workspace_size(q, H, 1, n, n, pv_mode=args.pv_mode, partials=args.partials)
+    ws_bytes = _lib.workspace_size(q, H, 1, n, n, nsplit=args.nsplit, pv_mode=args.pv_mode, partials=args.partials)
 
     host = {k: getattr(case, k) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
     if args.paged:
@@ -158,7 +162,7 @@ def main() -> int:
     # that host-side argument handling does not gap the back-to-back launches.
     # phase 0 = the whole call, 1 = the split kernel alone, 2 = the combine
     # kernel alone (on the workspace phase 1 filled).
-    opts = [_lib.options(0, args.pv_mode, 0, args.partials, ph) for ph in range(3)]
+    opts = [_lib.options(args.nsplit, args.pv_mode, 0, args.partials, ph) for ph in range(3)]
     entry = lib.mla_verify_paged if args.paged else lib.mla_verify_ex
     for d in copies:
         if args.paged:
@@ -278,7 +282,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tflops / (flops / (PAGES_US_Q9_P16384 * 1e-6) / 1e12), 2)
-        if args.workload == "q9_p16384" and H == 64 and not args.paged else None,
+        if args.workload == "q9_p16384" and H == 64 and not args.paged and args.prefix < 0 else None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": n, "heads": H, "dl": 512,

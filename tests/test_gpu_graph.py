@@ -1,0 +1,58 @@
+"""The verify call captured into a HIP graph (through torch.cuda.CUDAGraph)
+and replayed: the library launches kernels only (no allocation, no memset, no
+host synchronisation), so every replay must give the eager result bitwise.
+Inputs change between replays (copied into the captured buffers), with eager
+work and synchronisations in between."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from mla_tree_verify_amd import _lib, api, gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("prefix,nsplit", [(16384, 0), (256, 0), (300, 1)])
+def test_graph_replays_match_eager(prefix, nsplit):
+    cases = [gen.make_case(9, prefix, tree="random", seed=500 + k) for k in range(3)]
+    bufs = {k: getattr(cases[0], k).to(DEV) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
+    n = prefix + 9
+    ws = torch.zeros(max(16, _lib.workspace_size(9, 64, 1, n, n, nsplit=nsplit)), dtype=torch.uint8, device=DEV)
+    out = torch.empty(9, 64, 512, dtype=torch.float32, device=DEV)
+    lse = torch.empty(9, 64, dtype=torch.float32, device=DEV)
+
+    def call():
+        api.mla_verify(bufs["q_nope"], bufs["q_rope"], bufs["kv_latent"], bufs["k_rope"], bufs["tree_parent"],
+                       prefix, cases[0].scale, out=out, lse=lse, workspace=ws, nsplit=nsplit)
+
+    # eager references
+    refs = []
+    for c in cases:
+        for k in bufs:
+            bufs[k].copy_(getattr(c, k).to(DEV))
+        call()
+        torch.cuda.synchronize()
+        refs.append((out.clone(), lse.clone()))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(6):
+        k = rep % 3
+        for name in bufs:
+            bufs[name].copy_(getattr(cases[k], name).to(DEV))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, refs[k][0]) and torch.equal(lse, refs[k][1]), f"replay {rep} differs from eager"
+        # eager work between replays
+        torch.randn(1000, device=DEV).sum().item()
