@@ -557,7 +557,9 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     for (int m = 0; m < 4; ++m) vb[m] = kk * 1024 + 16 * (z0 ^ (4 * m)) + 8 * (i & 1);
   }
 
-  const uint64_t anc = ancestor_mask_lanes(par_lane, a.q, tok);
+  // a block of one token (heads a multiple of 64): the uniform walk; else per lane
+  const uint64_t anc = a.heads % kRows == 0 ? ancestor_mask_wave(par_lane, a.q, uniform(tok))
+                                            : ancestor_mask_lanes(par_lane, a.q, tok);
 
   const int partner = wave ^ 1;  // same head half, other dim half
   const KBases kb = make_kbases(lane & 31, half);
