@@ -52,6 +52,8 @@ def parse():
                          "by a seeded random permutation, through mla_verify_paged")
     ap.add_argument("--pool-extra", type=int, default=0, help="paged: pool rows beyond the workload's KV rows")
     ap.add_argument("--nsplit", type=int, default=0, help="force the KV split count (0: the planner's)")
+    ap.add_argument("--merge", type=int, default=0,
+                    help="0: the combine kernel (default), 1: plans of 2..4 splits merge in the split kernel")
     ap.add_argument("--prefix", type=int, default=-1, help="override the workload's prefix length")
     ap.add_argument("--heads", type=int, default=64,
                     help="query heads per token (the workload's shape with this head count; 64 is the metric's)")
@@ -139,9 +141,11 @@ def main() -> int:
     H = args.heads
     flops = orc.algorithmic_flops(case.tree_parent, p, num_heads=H)
     alg_bytes = orc.algorithmic_bytes(q, n, num_heads=H)
-    plan = api.device_plan(q, 1, n, n, nsplit=args.nsplit, pv_mode=args.pv_mode, num_heads=H)
+    plan = api.device_plan(q, 1, n, n, nsplit=args.nsplit, pv_mode=args.pv_mode, num_heads=H,
+                           partials=args.partials, merge=args.merge)
     lib = _lib.load()
-    ws_bytes = _lib.workspace_size(q, H, 1, n, n, nsplit=args.nsplit, pv_mode=args.pv_mode, partials=args.partials)
+    ws_bytes = _lib.workspace_size(q, H, 1, n, n, nsplit=args.nsplit, pv_mode=args.pv_mode, partials=args.partials,
+                                   merge=args.merge)
 
     host = {k: getattr(case, k) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
     if args.paged:
@@ -161,8 +165,9 @@ def main() -> int:
     # Each timed call goes straight to the C ABI with prebuilt arguments, so
     # that host-side argument handling does not gap the back-to-back launches.
     # phase 0 = the whole call, 1 = the split kernel alone, 2 = the combine
-    # kernel alone (on the workspace phase 1 filled).
-    opts = [_lib.options(args.nsplit, args.pv_mode, 0, args.partials, ph) for ph in range(3)]
+    # kernel alone (on the workspace phase 1 filled; nothing when the split
+    # kernel merges the splits itself).
+    opts = [_lib.options(args.nsplit, args.pv_mode, 0, args.partials, ph, args.merge) for ph in range(3)]
     entry = lib.mla_verify_paged if args.paged else lib.mla_verify_ex
     for d in copies:
         if args.paged:
@@ -229,7 +234,7 @@ def main() -> int:
         return e0.elapsed_time(e1) * 1e3 / args.steps
 
     split_us = batch_us(split)
-    combine_us = batch_us(merge) if plan.nsplit > 1 else 0.0
+    combine_us = batch_us(merge) if plan.combine == 1 else 0.0
 
     if args.copy_calib_mb > 0:
         nb = int(args.copy_calib_mb * 2**20) // 4 * 4
@@ -288,6 +293,7 @@ def main() -> int:
         "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": n, "heads": H, "dl": 512,
                    "dr": 64, "tree": case.meta["tree"], "scale": case.scale, "nsplit": plan.nsplit,
                    "chunk": plan.chunk, "pv_mode": args.pv_mode, "partials": "int16" if args.partials == 0 else "fp32",
+                   "merge": ["none (one split)", "combine kernel", "in the split kernel"][plan.combine],
                    "kv_layout": (f"paged, one token per page, pool {n + args.pool_extra} rows" if args.paged
                                  else "contiguous"),
                    "parallelism": "single GPU"},

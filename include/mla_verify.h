@@ -95,7 +95,19 @@ typedef struct mlav_options {
                        one split the partials stay in the workspace); 2: the
                        combine kernel only, on the workspace that a phase-1 call
                        with the same arguments filled (nothing runs when the plan
-                       has one split: phase 1 then wrote out and lse) */
+                       has one split or is merged in the split kernel: phase 1
+                       then wrote out and lse) */
+  int32_t merge;    /* 0 (the default): plans with more than one split run the
+                       combine kernel after the split kernel;
+                       1: a plan of 2..4 splits with int16 partials (short
+                       prefixes) is merged in the split kernel instead: the
+                       last workgroup of each row block to finish merges that
+                       block's splits, so the call is one launch
+                       (plan->combine = 2; the workspace then also holds one
+                       8-byte ticket per row block, which needs no clearing).
+                       On MI355X this is slower than the two launches (one CU
+                       pulls all partials of its row block, after two extra
+                       device-scope round trips), hence not the default */
 } mlav_options;
 
 /* What the planner decided for one call. */
@@ -104,7 +116,10 @@ typedef struct mlav_plan {
   int32_t tile;    /* keys per wave tile */
   int64_t chunk;   /* keys per split (a multiple of tile) */
   int32_t grid;    /* workgroups of the split kernel */
-  int32_t combine; /* 1 when the combine kernel runs (nsplit > 1) */
+  int32_t combine; /* 0: one split, the split kernel writes out and lse;
+                      1: the combine kernel runs after the split kernel;
+                      2: the split kernel merges the splits itself (see
+                         mlav_options.merge) */
 } mlav_plan;
 
 /*

@@ -39,7 +39,7 @@ EXPORTS = (
 
 class Options(ctypes.Structure):
     _fields_ = [("nsplit", c_int32), ("pv_mode", c_int32), ("kernel", c_int32), ("partials", c_int32),
-                ("phase", c_int32)]
+                ("phase", c_int32), ("merge", c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -102,14 +102,15 @@ def strerror(status: int) -> str:
     return load().mla_verify_strerror(status).decode()
 
 
-def options(nsplit: int = 0, pv_mode: int = 0, kernel: int = 0, partials: int = 0, phase: int = 0) -> Options:
-    return Options(nsplit, pv_mode, kernel, partials, phase)
+def options(nsplit: int = 0, pv_mode: int = 0, kernel: int = 0, partials: int = 0, phase: int = 0,
+            merge: int = 0) -> Options:
+    return Options(nsplit, pv_mode, kernel, partials, phase, merge)
 
 
 def plan(q_len: int, num_heads: int, batch: int, total_kv: int, max_kv: int, num_cus: int,
-         nsplit: int = 0, pv_mode: int = 0, kernel: int = 0) -> Plan:
+         nsplit: int = 0, pv_mode: int = 0, kernel: int = 0, partials: int = 0, merge: int = 0) -> Plan:
     p = Plan()
-    opt = options(nsplit, pv_mode, kernel)
+    opt = options(nsplit, pv_mode, kernel, partials, merge=merge)
     rc = load().mla_verify_plan(q_len, num_heads, batch, total_kv, max_kv, num_cus, ctypes.byref(opt),
                                 ctypes.byref(p))
     if rc != MLAV_OK:
@@ -118,8 +119,8 @@ def plan(q_len: int, num_heads: int, batch: int, total_kv: int, max_kv: int, num
 
 
 def workspace_size(q_len: int, num_heads: int, batch: int, total_kv: int, max_kv: int, num_cus: int = 0,
-                   nsplit: int = 0, pv_mode: int = 0, kernel: int = 0, partials: int = 0) -> int:
-    opt = options(nsplit, pv_mode, kernel, partials)
+                   nsplit: int = 0, pv_mode: int = 0, kernel: int = 0, partials: int = 0, merge: int = 0) -> int:
+    opt = options(nsplit, pv_mode, kernel, partials, merge=merge)
     return int(load().mla_verify_workspace_size(q_len, num_heads, batch, total_kv, max_kv, num_cus,
                                                  ctypes.byref(opt)))
 

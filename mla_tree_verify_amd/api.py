@@ -41,11 +41,14 @@ def mla_verify(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tens
                tree_parent: torch.Tensor, prefix_len: int, scale: float,
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None, nsplit: int = 0, pv_mode: int = 0,
-               kernel: int = 0, partials: int = 0, phase: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+               kernel: int = 0, partials: int = 0, phase: int = 0,
+               merge: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """One sequence: q_nope [q,H,512], q_rope [q,H,64], kv_latent [P+q,512], k_rope [P+q,64]
     (bf16), tree_parent [q] int32 -> out [q,H,512] fp32, lse [q,H] fp32.
     partials: 0 = int16 split partials with per-row scales (default), 1 = fp32.
-    phase: 0 = whole call, 1 = split kernel only, 2 = combine kernel only (same workspace)."""
+    phase: 0 = whole call, 1 = split kernel only, 2 = combine kernel only (same workspace).
+    merge: 0 = the combine kernel merges the splits (default), 1 = plans of 2..4 splits
+    merge in the split kernel (one launch)."""
     if not q_nope.is_cuda:
         raise ValueError("inputs must be on a GPU (the library has no CPU path)")
     dev = q_nope.device
@@ -63,7 +66,7 @@ def mla_verify(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tens
     _check(out, "out", torch.float32, (q, h, DL), dev)
     _check(lse, "lse", torch.float32, (q, h), dev)
     lib = _lib.load()
-    opt = _lib.options(nsplit, pv_mode, kernel, partials, phase)
+    opt = _lib.options(nsplit, pv_mode, kernel, partials, phase, merge)
     need = int(lib.mla_verify_workspace_size(q, h, 1, n, n, 0, ctypes.byref(opt)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -82,7 +85,7 @@ def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: to
                        scale: float, max_kv: Optional[int] = None,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, nsplit: int = 0, pv_mode: int = 0,
-                       kernel: int = 0, partials: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                       kernel: int = 0, partials: int = 0, merge: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """B sequences: q_nope [B,q,H,512], kv rows of sequence b = [off[b], off[b+1]),
     tree_parent [B,q] int32, kv_offsets [B+1] int64 (CPU or device)."""
     if not q_nope.is_cuda:
@@ -108,7 +111,7 @@ def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: to
     _check(out, "out", torch.float32, (bsz, q, h, DL), dev)
     _check(lse, "lse", torch.float32, (bsz, q, h), dev)
     lib = _lib.load()
-    opt = _lib.options(nsplit, pv_mode, kernel, partials)
+    opt = _lib.options(nsplit, pv_mode, kernel, partials, merge=merge)
     need = int(lib.mla_verify_workspace_size(q, h, bsz, total, max_kv, 0, ctypes.byref(opt)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -128,7 +131,7 @@ def mla_verify_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, pool_latent: to
                      kv_offsets: Optional[torch.Tensor] = None, max_kv: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, nsplit: int = 0, pv_mode: int = 0,
-                     kernel: int = 0, partials: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                     kernel: int = 0, partials: int = 0, merge: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged KV (one token per page): pool_latent [R,512], pool_rope [R,64] bf16,
     kv_index [N] int32 (logical row -> pool row). One sequence: q_nope [q,H,512],
     tree_parent [q], kv_offsets None (its N logical rows are its prefix then its
@@ -168,7 +171,7 @@ def mla_verify_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, pool_latent: to
     _check(out, "out", torch.float32, lead + (q, h, DL), dev)
     _check(lse, "lse", torch.float32, lead + (q, h), dev)
     lib = _lib.load()
-    opt = _lib.options(nsplit, pv_mode, kernel, partials)
+    opt = _lib.options(nsplit, pv_mode, kernel, partials, merge=merge)
     need = int(lib.mla_verify_workspace_size(q, h, bsz, total, int(max_kv), 0, ctypes.byref(opt)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -240,8 +243,8 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor,
 
 
 def device_plan(q_len: int, batch: int, total_kv: int, max_kv: int, nsplit: int = 0, pv_mode: int = 0,
-                kernel: int = 0, device=None, num_heads: int = H) -> _lib.Plan:
+                kernel: int = 0, device=None, num_heads: int = H, partials: int = 0, merge: int = 0) -> _lib.Plan:
     """The plan a call on `device` would use (reads the device's CU count)."""
     props = torch.cuda.get_device_properties(device if device is not None else torch.cuda.current_device())
     return _lib.plan(q_len, num_heads, batch, total_kv, max_kv, props.multi_processor_count, nsplit, pv_mode,
-                     kernel)
+                     kernel, partials, merge)

@@ -98,6 +98,8 @@ struct Args {
   int16_t* part_q;       // [B, S, q, H, 512] compact partials (int16 x part_scale)
   float* part_scale;     // [B, S, q, H]
   float* part_lse;       // [B, S, q, H]
+  unsigned long long* tickets;  // merge in the split kernel: [B, nrb] (epoch << 16 | arrivals)
+  unsigned long long epoch;     // this call's ticket epoch (48 bits, not 0)
   int64_t single_n;
   int64_t total_kv;
   int64_t max_kv;
@@ -443,7 +445,108 @@ __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&
 // tile load into one slot does not write the slots being read and issues no
 // wait for it), an 8 KB partial-score exchange and an 8 KB weight exchange:
 // 163840 bytes. A tile is loaded three steps ahead of its value product.
-template <int kDh, bool kHiLo, bool kCompact, bool kPaged>
+// Merge in the split kernel (plans of 2..4 splits): every workgroup of a row
+// block writes its partial rows with device-coherent stores (sc1: written
+// through the XCD's L2, whose lines other XCDs do not see), waits until they
+// are performed and takes a ticket; the one that takes the last ticket reads
+// the block's rows with device-coherent loads and merges them, so no combine
+// launch follows. A full release/acquire fence pair would instead write back
+// and invalidate the whole L2 of the XCD, which costs more than the merge.
+// A ticket word is (epoch << 16) | arrivals; a word from another epoch (a
+// previous call, or whatever the workspace held) counts as empty, and the
+// last arriver resets it to 0, so the workspace needs no clearing and a
+// replayed graph (same epoch) starts from 0 each time.
+constexpr int kMaxFusedSplits = 4;
+constexpr int kCoherent = 16;  // buffer cache policy: sc1 (device scope)
+template <int kNs>
+__device__ inline void merge_block(const Args& a, LDS_AS char* xs, int b, int rbk, int wave, int lane) {
+  constexpr int ns = kNs;
+  constexpr int kR = kNs == 2 ? 16 : 8;  // rows per round of loads (all of a round in flight)
+  unsigned long long* tk = a.tickets + (int64_t)b * a.nrb + rbk;
+  const int rows_seq = a.q * a.heads;
+  const int64_t out_row0 = (int64_t)b * rows_seq + rbk * kRows;  // first output row of the block
+  const int nvalid = rows_seq - rbk * kRows < kRows ? rows_seq - rbk * kRows : kRows;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent partial stores are performed
+  __syncthreads();                // (also: every wave is done with the exchange area)
+  if (threadIdx.x == 0) {
+    unsigned long long old = __hip_atomic_load(tk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int last = 0;
+    for (int tries = 0; tries < 64; ++tries) {  // at most ns - 1 concurrent updates can make a CAS fail
+      const unsigned long long nw = (old >> 16) == a.epoch ? old + 1 : (a.epoch << 16) | 1ull;
+      const unsigned long long seen = atomicCAS(tk, old, nw);
+      if (seen == old) {
+        last = (int)(nw & 0xFFFFull) == ns;
+        break;
+      }
+      old = seen;
+    }
+    *(LDS_AS int*)xs = last;
+  }
+  __syncthreads();
+  if (*(const LDS_AS int*)xs == 0) return;
+  // wave w merges rows [16 w, 16 w + 16) of the block, 8 at a time with every
+  // load in flight; lane l owns dims [8 l, 8 l + 8), lane s < ns fetches split
+  // s's lse and scale
+  const int sstride = a.nrb * kRows;
+  const int64_t row_base = ((int64_t)b * a.nsplit * a.nrb + rbk) * kRows;  // split 0, row 0 of the block
+  __amdgpu_buffer_rsrc_t rs[kNs];  // the block's 64 rows of each split
+#pragma unroll
+  for (int sp = 0; sp < kNs; ++sp)
+    rs[sp] = make_rsrc(a.part_q + (row_base + (int64_t)sp * sstride) * kDl, kRows * kDl * 2);
+#pragma unroll 1
+  for (int k0 = 0; k0 < 16; k0 += kR) {
+    u32x4_t qv[kR][kNs];
+    float lzs[kR], scs[kR];
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int h = 16 * wave + k0 + k;
+#pragma unroll
+      for (int sp = 0; sp < kNs; ++sp)
+        qv[k][sp] = __builtin_amdgcn_raw_buffer_load_b128(rs[sp], h * (kDl * 2) + 16 * lane, 0, kCoherent);
+      const int64_t rr = row_base + (int64_t)(lane < ns ? lane : 0) * sstride + h;
+      lzs[k] = __hip_atomic_load(a.part_lse + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      scs[k] = __hip_atomic_load(a.part_scale + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int h = 16 * wave + k0 + k;
+      float lz[kNs], sc[kNs];
+      float M = -INFINITY;
+#pragma unroll
+      for (int sp = 0; sp < kNs; ++sp) {
+        lz[sp] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lzs[k]), sp));
+        sc[sp] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scs[k]), sp));
+        M = fmax3(M, lz[sp]);
+      }
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float wsum = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int sp = 0; sp < kNs; ++sp) {
+          const float w = __builtin_amdgcn_exp2f((lz[sp] - M) * kLog2e);  // 0 for a split that saw no key
+          wsum += w;
+          const float f = w * sc[sp];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int32_t v = (int32_t)qv[k][sp][e];
+            acc[2 * e] += f * (float)((v << 16) >> 16);
+            acc[2 * e + 1] += f * (float)(v >> 16);
+          }
+        }
+      }
+      if (h < nvalid) {
+        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+        float* o = a.out + (out_row0 + h) * kDl + 8 * lane;
+        *(f32x4_t*)o = (f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv;
+        *(f32x4_t*)(o + 4) = (f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv;
+        if (lane == 0) a.lse[out_row0 + h] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+      }
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(tk, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int kDh, bool kHiLo, bool kCompact, bool kPaged, bool kFused>
 __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r1, LDS_AS char* r2,
                                   LDS_AS char* r3, LDS_AS char* xs, LDS_AS char* xp, int b, int s,
                                   int rbk, int wave, int hh, int lane, int64_t row0, int64_t n) {
@@ -907,6 +1010,10 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // leaves as one contiguous 1 KB store.
     LDS_AS char* slot = ring(lane >> 4);
     const int cl = 2 * (lane & 15);
+    // a block merged in this kernel is read by another workgroup: its rows
+    // are stored device-coherent
+    constexpr bool coherent = kFused;
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.part_q + prow * kDl, kRows * kDl * 2);
     float my_scale = 0.f;  // lane k < 16 keeps the scale of row 16 w + k
 #pragma unroll 4
     for (int k = 0; k < 16; ++k) {
@@ -924,12 +1031,21 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       auto q2 = [&](float x, float y) {
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(x * g, y * g));
       };
-      *(u32x4_t*)(a.part_q + (prow + h) * kDl + 8 * lane) =
-          (u32x4_t){q2(v0[0], v0[1]), q2(v0[2], v0[3]), q2(v1[0], v1[1]), q2(v1[2], v1[3])};
+      const u32x4_t pk = {q2(v0[0], v0[1]), q2(v0[2], v0[3]), q2(v1[0], v1[1]), q2(v1[2], v1[3])};
+      if (coherent)
+        __builtin_amdgcn_raw_buffer_store_b128(pk, prs, h * (kDl * 2) + 16 * lane, 0, kCoherent);
+      else
+        *(u32x4_t*)(a.part_q + (prow + h) * kDl + 8 * lane) = pk;
       const float sc = m * *(const LDS_AS float*)(xp + h * 4) * (1.f / 32767.f);
       my_scale = lane == k ? sc : my_scale;
     }
-    if (lane < 16) a.part_scale[prow + 16 * wave + lane] = my_scale;
+    if (lane < 16) {
+      if (coherent)
+        __hip_atomic_store(a.part_scale + prow + 16 * wave + lane, my_scale, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else
+        a.part_scale[prow + 16 * wave + lane] = my_scale;
+    }
   } else {
     float* obase = final_write ? a.out + out_row0 * kDl : a.part_o + prow * kDl;
     const int nstore = final_write ? nvalid : kRows;
@@ -947,12 +1063,15 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   if (kDh == 0 && half == 0) {
     if (final_write) {
       if (head < nvalid) a.lse[out_row0 + head] = lse_val;
-    } else
+    } else if (kFused) {
+      __hip_atomic_store(a.part_lse + prow + head, lse_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
       a.part_lse[prow + head] = lse_val;
+    }
   }
 }
 
-template <bool kHiLo, bool kCompact, bool kPaged>
+template <bool kHiLo, bool kCompact, bool kPaged, bool kFused>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_mfma_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char ring0[kTileBytes];
@@ -987,9 +1106,18 @@ void split_mfma_kernel(Args a) {
   if ((int64_t)s * a.chunk >= n) return;  // this sequence needs fewer splits
   const int hh = wave >> 1;
   if ((wave & 1) == 0)
-    split_body<0, kHiLo, kCompact, kPaged>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
+    split_body<0, kHiLo, kCompact, kPaged, kFused>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
   else
-    split_body<1, kHiLo, kCompact, kPaged>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
+    split_body<1, kHiLo, kCompact, kPaged, kFused>(a, r0, r1, r2, r3, xs, xp, b, s, t, wave, hh, lane, row0, n);
+  if constexpr (kFused) {
+    static_assert(kCompact, "the merge in the split kernel reads int16 partials");
+    switch ((int)((n + a.chunk - 1) / a.chunk)) {  // this sequence's splits
+      case 2: merge_block<2>(a, xs, b, t, wave, lane); break;
+      case 3: merge_block<3>(a, xs, b, t, wave, lane); break;
+      case 4: merge_block<4>(a, xs, b, t, wave, lane); break;
+      default: break;  // one split: out and lse are written
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1321,9 +1449,15 @@ int device_cus(int32_t* out) {
 int check_options(const mlav_options* opt) {
   if (!opt) return MLAV_OK;
   if (opt->nsplit < 0 || opt->pv_mode < 0 || opt->pv_mode > 1 || opt->kernel < 0 ||
-      opt->kernel > 1 || opt->partials < 0 || opt->partials > 1 || opt->phase < 0 || opt->phase > 2)
+      opt->kernel > 1 || opt->partials < 0 || opt->partials > 1 || opt->phase < 0 || opt->phase > 2 ||
+      opt->merge < 0 || opt->merge > 1)
     return MLAV_ERR_ARG;
   return MLAV_OK;
+}
+
+bool compact_partials(const mlav_options* opt) {
+  // the VALU cross-check kernel writes fp32 partials only
+  return (opt ? opt->partials : 0) == 0 && (opt ? opt->kernel : 0) == 0;
 }
 
 // Row blocks of one sequence: its q * heads (token, head) rows in blocks of 64.
@@ -1364,22 +1498,35 @@ int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t
   } else {
     p->grid = (int32_t)(nwork * 16);
   }
-  p->combine = ns > 1 ? 1 : 0;
+  // merge = 1, 2..kMaxFusedSplits splits and int16 partials: the split kernel
+  // merges them itself (one launch); otherwise the combine kernel runs
+  const bool fused = ns >= 2 && ns <= kMaxFusedSplits && compact_partials(opt) && (opt ? opt->merge : 0) == 1;
+  p->combine = ns > 1 ? (fused ? 2 : 1) : 0;
   return MLAV_OK;
 }
 
 // Split partials in the workspace: values, then lse, then (compact only) the
 // per-row scales, over [B, S, nrb * 64] rows (each sequence's q * heads rows
 // padded to whole row blocks). Compact values are int16: 1024 bytes per row.
-bool compact_partials(const mlav_options* opt) {
-  // the VALU cross-check kernel writes fp32 partials only
-  return (opt ? opt->partials : 0) == 0 && (opt ? opt->kernel : 0) == 0;
-}
+// A plan merged in the split kernel adds one 8-byte ticket per row block.
 
 size_t workspace_bytes_for(const mlav_plan& p, int32_t q, int32_t heads, int32_t batch, bool compact) {
   if (!p.combine) return 0;
   const size_t rows = (size_t)batch * p.nsplit * row_blocks(q, heads) * kRows;
-  return compact ? rows * (kDl * sizeof(int16_t) + 2 * sizeof(float)) : rows * (kDl + 1) * sizeof(float);
+  const size_t tickets = p.combine == 2 ? (size_t)batch * row_blocks(q, heads) * sizeof(uint64_t) : 0;
+  return compact ? rows * (kDl * sizeof(int16_t) + 2 * sizeof(float)) + tickets : rows * (kDl + 1) * sizeof(float);
+}
+
+// A fresh ticket epoch per call: 48 bits of a splitmix64 hash of a
+// process-wide counter, so a stale word in the workspace (old partial values,
+// another call's tickets) matches it with probability about 2^-48.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{0};
+  uint64_t z = counter.fetch_add(1, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z = (z ^ (z >> 31)) & ((uint64_t(1) << 48) - 1);
+  return z ? z : 1;
 }
 
 // Points the partial pointers of `a` into the workspace (layout above).
@@ -1390,11 +1537,17 @@ void set_partials(Args& a, void* workspace, const mlav_plan& p, int32_t q, int32
   a.part_q = nullptr;
   a.part_scale = nullptr;
   a.part_lse = nullptr;
+  a.tickets = nullptr;
+  a.epoch = 0;
   if (!p.combine) return;
   if (compact) {
     a.part_q = (int16_t*)workspace;
     a.part_lse = (float*)(a.part_q + rows * kDl);
     a.part_scale = a.part_lse + rows;
+    if (p.combine == 2) {
+      a.tickets = (unsigned long long*)(a.part_scale + rows);  // rows is a multiple of 64: 8-byte aligned
+      a.epoch = next_epoch();
+    }
   } else {
     a.part_o = (float*)workspace;
     a.part_lse = a.part_o + rows * kDl;
@@ -1421,11 +1574,17 @@ int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* 
     // one instantiation per (weight form, partial format, KV layout)
     using K = void (*)(Args);
     static const K table[2][2][2] = {
-        {{split_mfma_kernel<true, false, false>, split_mfma_kernel<true, false, true>},
-         {split_mfma_kernel<true, true, false>, split_mfma_kernel<true, true, true>}},
-        {{split_mfma_kernel<false, false, false>, split_mfma_kernel<false, false, true>},
-         {split_mfma_kernel<false, true, false>, split_mfma_kernel<false, true, true>}}};
-    const K k = table[pv_mode == 0 ? 0 : 1][compact ? 1 : 0][a.idx ? 1 : 0];
+        {{split_mfma_kernel<true, false, false, false>, split_mfma_kernel<true, false, true, false>},
+         {split_mfma_kernel<true, true, false, false>, split_mfma_kernel<true, true, true, false>}},
+        {{split_mfma_kernel<false, false, false, false>, split_mfma_kernel<false, false, true, false>},
+         {split_mfma_kernel<false, true, false, false>, split_mfma_kernel<false, true, true, false>}}};
+    // merged in the split kernel: its own instantiations, so that the other
+    // kernels carry none of its code
+    static const K fused_table[2][2] = {
+        {split_mfma_kernel<true, true, false, true>, split_mfma_kernel<true, true, true, true>},
+        {split_mfma_kernel<false, true, false, true>, split_mfma_kernel<false, true, true, true>}};
+    const K k = p.combine == 2 ? fused_table[pv_mode == 0 ? 0 : 1][a.idx ? 1 : 0]
+                               : table[pv_mode == 0 ? 0 : 1][compact ? 1 : 0][a.idx ? 1 : 0];
     hipLaunchKernelGGL(k, dim3(p.grid), dim3(kThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL(split_valu_kernel, dim3(p.grid), dim3(kThreads), 0, st, a);
@@ -1433,7 +1592,7 @@ int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* 
   if (hipGetLastError() != hipSuccess) return MLAV_ERR_HIP;
   if (phase == 1) return MLAV_OK;
 merge:
-  if (p.combine) {
+  if (p.combine == 1) {
     const int64_t rows = (int64_t)a.batch * a.q * a.heads;
     if (compact) {
       if (p.nsplit <= 32)

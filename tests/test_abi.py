@@ -93,6 +93,33 @@ def test_workspace_size(lib):
     assert _lib.workspace_size(0, 64, 1, n, n, num_cus=256) == 0
 
 
+def test_plan_merged_in_split_kernel(lib):
+    """With merge = 1, plans of 2..4 splits with int16 partials merge in the
+    split kernel (combine = 2) and add one 8-byte ticket per row block to the
+    workspace; merge = 0 (the default), fp32 partials or the VALU kernel keep
+    the combine kernel."""
+    for n, ns in [(200, 2), (300, 3), (500, 4)]:
+        pl = _lib.plan(9, 64, 1, n, n, 256, merge=1)
+        assert pl.nsplit == ns and pl.combine == 2
+        ws = _lib.workspace_size(9, 64, 1, n, n, num_cus=256, merge=1)
+        assert ws == ns * 9 * 64 * (512 * 2 + 8) + 9 * 8
+        pl0 = _lib.plan(9, 64, 1, n, n, 256)
+        assert pl0.nsplit == ns and pl0.combine == 1
+        assert _lib.workspace_size(9, 64, 1, n, n, num_cus=256) == ns * 9 * 64 * (512 * 2 + 8)
+        assert _lib.plan(9, 64, 1, n, n, 256, partials=1, merge=1).combine == 1
+        assert _lib.plan(9, 64, 1, n, n, 256, kernel=1, merge=1).combine == 1
+    # 5 or more splits: the combine kernel
+    pl5 = _lib.plan(9, 64, 1, 600, 600, 256, merge=1)
+    assert pl5.nsplit == 5 and pl5.combine == 1
+    # batched, any head count: tickets for every (sequence, row block)
+    pl = _lib.plan(9, 8, 3, 3 * 300, 300, 256, merge=1)
+    assert pl.combine == 2
+    assert (_lib.workspace_size(9, 8, 3, 900, 300, num_cus=256, merge=1)
+            == 3 * pl.nsplit * 2 * 64 * (512 * 2 + 8) + 3 * 2 * 8)
+    # one split: no workspace, no combine
+    assert _lib.plan(9, 64, 1, 100, 100, 256, merge=1).combine == 0
+
+
 def test_plan_errors(lib):
     with pytest.raises(_lib.MLAVError) as e:
         _lib.plan(9, 1025, 1, 100, 100, 256)
@@ -140,7 +167,8 @@ def test_host_validation_errors(lib):
     assert call(lib, scale=0.0) == _lib.MLAV_ERR_ARG
     assert call(lib, scale=-0.5) == _lib.MLAV_ERR_ARG
     for bad in (_lib.Options(0, 0, 0, 2, 0), _lib.Options(0, 0, 0, -1, 0), _lib.Options(0, 0, 0, 0, 3),
-                _lib.Options(0, 0, 2, 0, 0), _lib.Options(0, 2, 0, 0, 0), _lib.Options(-1, 0, 0, 0, 0)):
+                _lib.Options(0, 0, 2, 0, 0), _lib.Options(0, 2, 0, 0, 0), _lib.Options(-1, 0, 0, 0, 0),
+                _lib.Options(0, 0, 0, 0, 0, 2), _lib.Options(0, 0, 0, 0, 0, -1)):
         assert lib.mla_verify_ex(A, A, A, A, A, 100, 0.07, A, A, 9, 64, None, 0, None,
                                  ctypes.byref(bad)) == _lib.MLAV_ERR_ARG
 

@@ -14,18 +14,21 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("prefix,nsplit", [(16384, 0), (256, 0), (300, 1)])
-def test_graph_replays_match_eager(prefix, nsplit):
+@pytest.mark.parametrize("prefix,nsplit,merge", [(16384, 0, 0), (256, 0, 0), (256, 0, 1), (300, 1, 0)])
+def test_graph_replays_match_eager(prefix, nsplit, merge):
+    """merge = 1 at prefix 256: the split kernel merges its 3 splits (tickets
+    in the workspace, reset by the last workgroup, same epoch on every replay)."""
     cases = [gen.make_case(9, prefix, tree="random", seed=500 + k) for k in range(3)]
     bufs = {k: getattr(cases[0], k).to(DEV) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
     n = prefix + 9
-    ws = torch.zeros(max(16, _lib.workspace_size(9, 64, 1, n, n, nsplit=nsplit)), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(16, _lib.workspace_size(9, 64, 1, n, n, nsplit=nsplit, merge=merge)), dtype=torch.uint8,
+                     device=DEV)
     out = torch.empty(9, 64, 512, dtype=torch.float32, device=DEV)
     lse = torch.empty(9, 64, dtype=torch.float32, device=DEV)
 
     def call():
         api.mla_verify(bufs["q_nope"], bufs["q_rope"], bufs["kv_latent"], bufs["k_rope"], bufs["tree_parent"],
-                       prefix, cases[0].scale, out=out, lse=lse, workspace=ws, nsplit=nsplit)
+                       prefix, cases[0].scale, out=out, lse=lse, workspace=ws, nsplit=nsplit, merge=merge)
 
     # eager references
     refs = []
