@@ -973,80 +973,99 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   __syncthreads();
   l_tot += *(const LDS_AS float*)(xs + partner * 2048 + lane * 4);
 
-  // Stage the accumulators through LDS so that each global store writes two
-  // 512-byte row pieces instead of 32-byte pieces of 32 rows. Ring slot o
-  // takes dims [128 o, 128 o + 128) of all 64 rows (the slot of a write is
-  // then a compile-time choice); row h's 32 16-byte chunks sit at
-  // h * 512 + 16 * (c ^ (h & 15)), conflict-free for the row-per-lane writes
-  // and the chunk-per-lane reads. The reads apply 1 / l, kept per row in
-  // the weight-exchange area. Partials keep the padded row block (all 64
-  // rows); the final output takes the block's rows below q * heads only.
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_val = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   const bool final_write = nsplit_b == 1;
   const bool compact = kCompact && !final_write;
-  if (kDh == 0 && half == 0) *(LDS_AS float*)(xp + head * 4) = inv;
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    LDS_AS char* slot = ring(2 * kDh + (db >> 2));
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int c = 8 * (db & 3) + 2 * g + half;
-      *(LDS_AS f32x4_t*)(slot + head * 512 + 16 * (c ^ (head & 15))) =
-          (f32x4_t){acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
-    }
-  }
-  __syncthreads();
   const int64_t out_row0 = (int64_t)b * rows_seq + rbk * kRows;  // first output row of the block
   const int nvalid = rows_seq - rbk * kRows < kRows ? rows_seq - rbk * kRows : kRows;
   const int64_t prow = (((int64_t)b * a.nsplit + s) * a.nrb + rbk) * kRows;  // first partial row
+  // Partials keep the padded row block (all 64 rows); the final output takes
+  // the block's rows below q * heads only.
   if (compact) {
-    // Compact partials: row h of the normalised partial is stored
-    // as 512 int16 values q with one fp32 scale, value = q * scale, where
-    // scale = (largest |value| of the row) / 32767; rounding to nearest keeps
-    // every value within scale / 2, i.e. 2^-16 of the row's largest. Wave w
-    // handles rows [16 w, 16 w + 16) whole; lane l holds dims [8 l, 8 l + 8)
-    // (ring slot l >> 4), so the row max is one wave reduction and each row
-    // leaves as one contiguous 1 KB store.
-    LDS_AS char* slot = ring(lane >> 4);
-    const int cl = 2 * (lane & 15);
-    // a block merged in this kernel is read by another workgroup: its rows
-    // are stored device-coherent
-    constexpr bool coherent = kFused;
+    // Compact partials: row h of the normalised partial is stored as 512
+    // int16 values q with one fp32 scale, value = q * scale, where scale =
+    // (largest |value| of the row) / 32767; rounding to nearest keeps every
+    // value within scale / 2, i.e. 2^-16 of the row's largest.
+    // The quantisation runs in the accumulator layout: lane (head, half)
+    // holds dims 256 kDh + 32 db + 8 g + 4 half + e of its row in acc[db][4 g
+    // + e], so the row max is an in-lane max, one lane-pair swap and one
+    // exchange with the partner wave (the other 256 dims), and adjacent dims
+    // sit in adjacent elements, which v_cvt_pknorm_i16_f32 packs pairwise.
+    // One lane-pair swap per two 8-byte pieces makes 16-byte chunks of 8
+    // dims (the lower lane takes g = 2 gp, the upper g = 2 gp + 1). Rows are
+    // staged in int16 (row h in ring slot h >> 5 at (h & 31) * 1024, 16-byte
+    // chunk j at 16 (j ^ (h & 31))) and leave as one 1 KB store per row.
+    float mx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2)
+        mx[(e >> 1) & 3] = fmax3(mx[(e >> 1) & 3], fmax3(__builtin_fabsf(acc[db][e]), __builtin_fabsf(acc[db][e + 1])));
+    float m = partner_max(fmax3(fmax3(mx[0], mx[1]), fmax3(mx[2], mx[3])));
+    *(LDS_AS float*)(xs + wave * 2048 + 1024 + lane * 4) = m;  // clear of the l_tot words read above
+    __syncthreads();
+    m = fmax3(m, *(const LDS_AS float*)(xs + partner * 2048 + 1024 + lane * 4));  // largest |acc| of the row
+    // acc / m lies in [-1, 1]; v_cvt_pknorm_i16_f32 scales by 32767, rounds
+    // to nearest and packs two values
+    const float g = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+    auto q2 = [&](float x, float y) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(x * g, y * g));
+    };
+    const int hs = lane & 31;  // head & 31
+    LDS_AS char* st = ring(hh) + hs * 1024;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const uint32_t a0 = q2(acc[db][8 * gp], acc[db][8 * gp + 1]);
+        const uint32_t a1 = q2(acc[db][8 * gp + 2], acc[db][8 * gp + 3]);
+        const uint32_t b0 = q2(acc[db][8 * gp + 4], acc[db][8 * gp + 5]);
+        const uint32_t b1 = q2(acc[db][8 * gp + 6], acc[db][8 * gp + 7]);
+        const auto x = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        const int j = 32 * kDh + 4 * db + 2 * gp + half;
+        *(LDS_AS u32x4_t*)(st + 16 * (j ^ hs)) = (u32x4_t){x[0], y[0], x[1], y[1]};
+      }
+    }
+    // The partial rows leave with device-scope stores (sc1: written through
+    // the XCD's L2). A block merged in this kernel needs that (another
+    // workgroup, maybe on another XCD, reads the rows at once); for the
+    // combine kernel it is measured 1 us faster per call at q 9, H 64,
+    // prefix 16384 than write-back stores, whose dirty lines the release at
+    // the kernel's end must write back before the combine can start.
+    if (kDh == 0 && half == 0)
+      __hip_atomic_store(a.part_scale + prow + head, m * inv * (1.f / 32767.f), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
     const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.part_q + prow * kDl, kRows * kDl * 2);
-    float my_scale = 0.f;  // lane k < 16 keeps the scale of row 16 w + k
-#pragma unroll 4
+    LDS_AS char* src = ring(wave >> 1);  // rows 16 wave .. 16 wave + 15 lie in slot wave >> 1
+#pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int h = 16 * wave + k;
-      const f32x4_t v0 = *(const LDS_AS f32x4_t*)(slot + h * 512 + 16 * (cl ^ k));
-      const f32x4_t v1 = *(const LDS_AS f32x4_t*)(slot + h * 512 + 16 * ((cl + 1) ^ k));
-      float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v0[0]), __builtin_fabsf(v0[1])),
-                                __builtin_fmaxf(__builtin_fabsf(v0[2]), __builtin_fabsf(v0[3])));
-      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v1[0]), __builtin_fabsf(v1[1])),
-                                             __builtin_fmaxf(__builtin_fabsf(v1[2]), __builtin_fabsf(v1[3]))));
-      m = wave_max(m);  // largest |acc| of the row (unnormalised)
-      // v / m lies in [-1, 1]; v_cvt_pknorm_i16_f32 scales by 32767, rounds
-      // to nearest and packs two values
-      const float g = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
-      auto q2 = [&](float x, float y) {
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(x * g, y * g));
-      };
-      const u32x4_t pk = {q2(v0[0], v0[1]), q2(v0[2], v0[3]), q2(v1[0], v1[1]), q2(v1[2], v1[3])};
-      if (coherent)
-        __builtin_amdgcn_raw_buffer_store_b128(pk, prs, h * (kDl * 2) + 16 * lane, 0, kCoherent);
-      else
-        *(u32x4_t*)(a.part_q + (prow + h) * kDl + 8 * lane) = pk;
-      const float sc = m * *(const LDS_AS float*)(xp + h * 4) * (1.f / 32767.f);
-      my_scale = lane == k ? sc : my_scale;
-    }
-    if (lane < 16) {
-      if (coherent)
-        __hip_atomic_store(a.part_scale + prow + 16 * wave + lane, my_scale, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      else
-        a.part_scale[prow + 16 * wave + lane] = my_scale;
+      const u32x4_t v = *(const LDS_AS u32x4_t*)(src + (h & 31) * 1024 + 16 * (lane ^ (h & 31)));
+      __builtin_amdgcn_raw_buffer_store_b128(v, prs, h * (kDl * 2) + 16 * lane, 0, kCoherent);
     }
   } else {
+    // Stage the accumulators through LDS so that each global store writes
+    // two 512-byte row pieces instead of 32-byte pieces of 32 rows. Ring
+    // slot o takes dims [128 o, 128 o + 128) of all 64 rows (the slot of a
+    // write is then a compile-time choice); row h's 32 16-byte chunks sit at
+    // h * 512 + 16 * (c ^ (h & 15)), conflict-free for the row-per-lane
+    // writes and the chunk-per-lane reads. The reads apply 1 / l, kept per
+    // row in the weight-exchange area.
+    if (kDh == 0 && half == 0) *(LDS_AS float*)(xp + head * 4) = inv;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      LDS_AS char* slot = ring(2 * kDh + (db >> 2));
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 8 * (db & 3) + 2 * g + half;
+        *(LDS_AS f32x4_t*)(slot + head * 512 + 16 * (c ^ (head & 15))) =
+            (f32x4_t){acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+      }
+    }
+    __syncthreads();
     float* obase = final_write ? a.out + out_row0 * kDl : a.part_o + prow * kDl;
     const int nstore = final_write ? nvalid : kRows;
     // this wave stores ring slot `wave`: dims [128 wave, 128 wave + 128)
@@ -1063,7 +1082,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   if (kDh == 0 && half == 0) {
     if (final_write) {
       if (head < nvalid) a.lse[out_row0 + head] = lse_val;
-    } else if (kFused) {
+    } else if (kCompact) {
       __hip_atomic_store(a.part_lse + prow + head, lse_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       a.part_lse[prow + head] = lse_val;
