@@ -633,16 +633,36 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   int par_lane;
   // resident queries for this wave's dim half: B operand of S^T = K Q^T
   bf16x8_t qreg[18];
-  first_tiles([&]() {
-    par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
-    const int64_t qrow = (int64_t)b * rows_seq + r_src;
+  if constexpr (kPaged) {
+    first_tiles([&]() {
+      par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
+      const int64_t qrow = (int64_t)b * rows_seq + r_src;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const int d = 288 * kDh + 16 * ks + 8 * half;
-      qreg[ks] = d < kDl ? *(const bf16x8_t*)(a.qn + qrow * kDl + d)
-                         : *(const bf16x8_t*)(a.qr + qrow * kDr + (d - kDl));
-    }
-  });
+      for (int ks = 0; ks < 18; ++ks) {
+        const int d = 288 * kDh + 16 * ks + 8 * half;
+        qreg[ks] = d < kDl ? *(const bf16x8_t*)(a.qn + qrow * kDl + d)
+                           : *(const bf16x8_t*)(a.qr + qrow * kDr + (d - kDl));
+      }
+    });
+  } else {
+    // The block's 64 query rows arrive like two key tiles (whole 1 KB rows
+    // per load, where loading the operand layout directly would touch 32
+    // rows per load): rows 0..31 into ring slot 3, rows 32..63 into slot 2,
+    // both in the tile layout, so that each wave reads its operand with the
+    // K-operand pattern. Rows past the block's valid rows read as zeros.
+    // Tile 2 is requested once every wave has its queries (slot 2 free).
+    issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+    __builtin_amdgcn_sched_barrier(0);
+    par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
+    const int64_t qrow0 = (int64_t)b * rows_seq + rbk * kRows;
+    const int qvalid = rows_seq - rbk * kRows < kRows ? rows_seq - rbk * kRows : kRows;
+    const __amdgpu_buffer_rsrc_t qn_rs = make_rsrc(a.qn + qrow0 * kDl, (uint32_t)qvalid * (kDl * 2));
+    const __amdgpu_buffer_rsrc_t qr_rs = make_rsrc(a.qr + qrow0 * kDr, (uint32_t)qvalid * (kDr * 2));
+    issue_tile(r3, qn_rs, qr_rs, 0, wave, lane, rope_voff);
+    issue_tile(r2, qn_rs, qr_rs, 32, wave, lane, rope_voff);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_tile(r1, lat_rs, rope_rs, tile_rel(1), wave, lane, rope_voff);
+  }
 
   // V^T operand (transposing reads): in each 16-lane group lane i reads 4
   // dims (16 dhalf + 4 (i&3) ..) of key row kk = 4 half + (i>>2) (+8 v for
@@ -709,9 +729,25 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // tile 0 landed; tiles 1, 2 (and the fourth tile's page-table entries) may be in flight
     if (kPaged)
       __builtin_amdgcn_s_waitcnt(0x4F73);  // vmcnt(19)
+    else if (attempt == 0)
+      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): tile 0 and the queries landed, tile 1 in flight
     else
       __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18)
     __syncthreads();
+    if constexpr (!kPaged) {
+      if (attempt == 0) {
+        // rows 32 hh .. 32 hh + 31 of the block, this wave's dim half
+        if (hh == 0) {
+#pragma unroll
+          for (int ks = 0; ks < 18; ++ks) qreg[ks] = lds_b128(r3 + k_frag_off<kDh>(kb, ks));
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 18; ++ks) qreg[ks] = lds_b128(r2 + k_frag_off<kDh>(kb, ks));
+        }
+        __syncthreads();  // every wave holds its queries: slots 2 and 3 are free
+        issue_tile(r2, lat_rs, rope_rs, tile_rel(2), wave, lane, rope_voff);
+      }
+    }
     const f32x16_t s0 = tile_scores<kDh>(r0, qreg, kb);
     float own[8];  // this wave's elements of the next tile's partial scores
 #pragma unroll
@@ -721,7 +757,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       for (int c = 0; c < 4; ++c)
         *(LDS_AS f32x4_t*)(r3 + wave * 4096 + c * 1024 + lane * 16) =
             (f32x4_t){s0[4 * c], s0[4 * c + 1], s0[4 * c + 2], s0[4 * c + 3]};
-      __syncthreads();
+      lds_barrier();  // (tile 2 may be in flight: no fence)
       const uint32_t vis0 = tile_visibility(c0, c1, prefix, anc);
       float mx = -INFINITY;
 #pragma unroll
