@@ -610,13 +610,13 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       issue_tile_part_paged(buf, lat_rs, rope_rs, idx_lane, ri, wave, lane, rope_loff, part);
   };
   int idx_cur = -1;  // paged: raw page-table entries of the next tile to load
-  // the first three tiles; paged KV reads their page-table entries first and
-  // the fourth tile's between tiles 1 and 2 (the same ten loads as a step)
-  auto first_tiles = [&](auto&& between) {
+  // the first three tiles again, for the redo after a reference-max
+  // overflow; paged KV reads their page-table entries first and the fourth
+  // tile's between tiles 1 and 2 (the same ten loads as a step)
+  auto restart_tiles = [&]() {
     if constexpr (kPaged) {
       const int i0 = load_idx(0), i1 = load_idx(1), i2 = load_idx(2);
       issue_paged(r0, checked_idx(0, i0));
-      between();
       issue_paged(r1, checked_idx(1, i1));
       __builtin_amdgcn_sched_barrier(0);
       idx_cur = load_idx(3);
@@ -624,7 +624,6 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       issue_paged(r2, checked_idx(2, i2));
     } else {
       issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
-      between();
       issue_tile(r1, lat_rs, rope_rs, tile_rel(1), wave, lane, rope_voff);
       issue_tile(r2, lat_rs, rope_rs, tile_rel(2), wave, lane, rope_voff);
     }
@@ -633,25 +632,26 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   int par_lane;
   // resident queries for this wave's dim half: B operand of S^T = K Q^T
   bf16x8_t qreg[18];
-  if constexpr (kPaged) {
-    first_tiles([&]() {
-      par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
-      const int64_t qrow = (int64_t)b * rows_seq + r_src;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const int d = 288 * kDh + 16 * ks + 8 * half;
-        qreg[ks] = d < kDl ? *(const bf16x8_t*)(a.qn + qrow * kDl + d)
-                           : *(const bf16x8_t*)(a.qr + qrow * kDr + (d - kDl));
-      }
-    });
-  } else {
-    // The block's 64 query rows arrive like two key tiles (whole 1 KB rows
-    // per load, where loading the operand layout directly would touch 32
-    // rows per load): rows 0..31 into ring slot 3, rows 32..63 into slot 2,
-    // both in the tile layout, so that each wave reads its operand with the
-    // K-operand pattern. Rows past the block's valid rows read as zeros.
-    // Tile 2 is requested once every wave has its queries (slot 2 free).
-    issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+  // The block's 64 query rows arrive like two key tiles (whole 1 KB rows per
+  // load, where loading the operand layout directly would touch 32 rows per
+  // load): rows 0..31 into ring slot 3, rows 32..63 into slot 2, both in the
+  // tile layout, so that each wave reads its operand with the K-operand
+  // pattern. Rows past the block's valid rows read as zeros. Tile 2 is
+  // requested once every wave holds its queries (slot 2 free). Issue order:
+  // tile 0, the parents, the queries, tile 1 (paged: the fourth tile's
+  // page-table entries after it), so that one vmcnt covers tile 0 and the
+  // queries.
+  int idx2 = -1;  // paged: raw page-table entries of tile 2
+  {
+    int i1 = -1;
+    if constexpr (kPaged) {
+      const int i0 = load_idx(0);
+      i1 = load_idx(1);
+      idx2 = load_idx(2);
+      issue_paged(r0, checked_idx(0, i0));
+    } else {
+      issue_tile(r0, lat_rs, rope_rs, 0, wave, lane, rope_voff);
+    }
     __builtin_amdgcn_sched_barrier(0);
     par_lane = lane < a.q ? a.parent[(int64_t)b * a.q + lane] : -1;
     const int64_t qrow0 = (int64_t)b * rows_seq + rbk * kRows;
@@ -661,7 +661,14 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     issue_tile(r3, qn_rs, qr_rs, 0, wave, lane, rope_voff);
     issue_tile(r2, qn_rs, qr_rs, 32, wave, lane, rope_voff);
     __builtin_amdgcn_sched_barrier(0);
-    issue_tile(r1, lat_rs, rope_rs, tile_rel(1), wave, lane, rope_voff);
+    if constexpr (kPaged) {
+      issue_paged(r1, checked_idx(1, i1));
+      __builtin_amdgcn_sched_barrier(0);
+      idx_cur = load_idx(3);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      issue_tile(r1, lat_rs, rope_rs, tile_rel(1), wave, lane, rope_voff);
+    }
   }
 
   // V^T operand (transposing reads): in each 16-lane group lane i reads 4
@@ -725,29 +732,35 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // prologue: tiles 0..2 in flight; tile 0's partial scores exchanged in
     // full (through ring slot 3, free until tile 3 is loaded) to fix m_ref,
     // then its partner half published for step 0
-    if (attempt == 1) first_tiles([]() {});
     // tile 0 landed; tiles 1, 2 (and the fourth tile's page-table entries) may be in flight
-    if (kPaged)
-      __builtin_amdgcn_s_waitcnt(0x4F73);  // vmcnt(19)
-    else if (attempt == 0)
-      __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): tile 0 and the queries landed, tile 1 in flight
-    else
-      __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18)
-    __syncthreads();
-    if constexpr (!kPaged) {
-      if (attempt == 0) {
-        // rows 32 hh .. 32 hh + 31 of the block, this wave's dim half
-        if (hh == 0) {
+    if (attempt == 0) {
+      // tile 0 and the queries landed; tile 1 (paged: and the fourth tile's
+      // page-table entries) may be in flight
+      if (kPaged)
+        __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+      __syncthreads();
+      // rows 32 hh .. 32 hh + 31 of the block, this wave's dim half
+      if (hh == 0) {
 #pragma unroll
-          for (int ks = 0; ks < 18; ++ks) qreg[ks] = lds_b128(r3 + k_frag_off<kDh>(kb, ks));
-        } else {
+        for (int ks = 0; ks < 18; ++ks) qreg[ks] = lds_b128(r3 + k_frag_off<kDh>(kb, ks));
+      } else {
 #pragma unroll
-          for (int ks = 0; ks < 18; ++ks) qreg[ks] = lds_b128(r2 + k_frag_off<kDh>(kb, ks));
-        }
-        __syncthreads();  // every wave holds its queries: slots 2 and 3 are free
-        issue_tile(r2, lat_rs, rope_rs, tile_rel(2), wave, lane, rope_voff);
+        for (int ks = 0; ks < 18; ++ks) qreg[ks] = lds_b128(r2 + k_frag_off<kDh>(kb, ks));
       }
+      __syncthreads();  // every wave holds its queries: slots 2 and 3 are free
     }
+    // tile 2 (in the redo: again, the same bytes; outside the branch so that
+    // the compiler's LDS-DMA tracking keeps the first steps' waits relaxed)
+    if constexpr (kPaged)
+      issue_paged(r2, checked_idx(2, idx2));
+    else
+      issue_tile(r2, lat_rs, rope_rs, tile_rel(2), wave, lane, rope_voff);
+    // (the redo's first tiles were loaded and drained at the end of the
+    // first attempt: no load crosses the back edge, so that at this join the
+    // compiler's LDS-DMA tracking still tells the ring slots apart and keeps
+    // the waits of the first steps relaxed)
     const f32x16_t s0 = tile_scores<kDh>(r0, qreg, kb);
     float own[8];  // this wave's elements of the next tile's partial scores
 #pragma unroll
@@ -999,6 +1012,10 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     __syncthreads();
     m_ref = fmax3(m_seen, *(const LDS_AS float*)(xs + partner * 2048 + lane * 4));
     have_ref = true;
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    restart_tiles();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tiles 0..2 (paged: and the fourth tile's entries) landed
     __syncthreads();
   }
 
