@@ -1335,12 +1335,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
 }
 
 // Combine of compact (int16 + scale) partials, up to 32 splits: one wave per
-// row; lane l owns dims [8 l, 8 l + 8), one 16-byte load per split, and all
+// row, one row per workgroup (the rows spread over every CU; at short
+// prefixes this launch is latency-bound, and four-wave workgroups left half
+// the CUs idle); lane l owns dims [8 l, 8 l + 8), one 16-byte load per split, and all
 // loads of a row are in flight together (one memory round trip). Lanes 0..31
 // fetch the lse and scale values, the max and weight sum come from 32-lane
 // reductions, and each split's weight * scale reaches all lanes by readlane.
-__global__ __launch_bounds__(kThreads) void combine_compact_kernel(Args a, int64_t rows) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(64) void combine_compact_kernel(Args a, int64_t rows) {
+  const int64_t row = blockIdx.x;
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
   const int64_t rows_b = (int64_t)a.q * a.heads;   // output rows per sequence
@@ -1390,8 +1392,10 @@ __global__ __launch_bounds__(kThreads) void combine_compact_kernel(Args a, int64
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv;
-  *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv;
+  // streaming stores: the rows are not read again by this GPU before the call ends
+  __builtin_nontemporal_store((f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv, (f32x4_t*)(a.out + row * kDl + 8 * lane));
+  __builtin_nontemporal_store((f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv,
+                              (f32x4_t*)(a.out + row * kDl + 8 * lane + 4));
   if (lane == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
 
@@ -1668,7 +1672,7 @@ merge:
     const int64_t rows = (int64_t)a.batch * a.q * a.heads;
     if (compact) {
       if (p.nsplit <= 32)
-        hipLaunchKernelGGL(combine_compact_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, a, rows);
+        hipLaunchKernelGGL(combine_compact_kernel, dim3((unsigned)rows), dim3(64), 0, st, a, rows);
       else
         hipLaunchKernelGGL(combine_compact_wide_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, rows);
     } else {
