@@ -72,7 +72,14 @@ static_assert(kLdsBytes <= 163840, "LDS per workgroup");
 constexpr int kXcds = 8;
 constexpr int64_t kChunkGran = kTile;
 constexpr int64_t kMinChunk = 128;
-constexpr float kRefHeadroom = 64.0f;  // log2 units: weights stay below 2^64
+// Reference max placement, log2 units: the reference sits kRefShift above
+// the first tile's max, so that tile's largest weight is 2^-32 and weights
+// may grow to 2^96 (scores up to 128 above that max) before a redo; keys more
+// than 94 below the max underflow to 0, a relative contribution below 2^-94.
+// With weights at most 2^96, the accumulators stay finite while
+// (keys in the chunk) x max|value| < 2^32.
+constexpr float kRefShift = 32.0f;
+constexpr float kRefHeadroom = 96.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -706,11 +713,14 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   };
 
   // Online softmax with a reference max that never moves inside the loop:
-  // the first tile with a visible key fixes it (the max of that tile's full
-  // scores, the same in all four waves), later weights are 2^(s - m_ref),
-  // exact for any m_ref. A score more than kRefHeadroom above m_ref could
-  // overflow; then the chunk is redone once with m_ref = the chunk's observed
-  // max, which no score exceeds. The accumulator is never rescaled.
+  // the first tile with a visible key fixes it (kRefShift above the max of
+  // that tile's full scores, the same in all four waves), later weights are
+  // 2^(s - m_ref), exact for any m_ref. A score more than kRefHeadroom above
+  // m_ref could overflow; then the chunk is redone once with m_ref = the
+  // chunk's observed max, which no score exceeds. The accumulator is never
+  // rescaled. (With the reference at the first tile's max and a headroom of
+  // 2^64, keys scaled by 8 in 1 % of the rows made most workgroups redo their
+  // chunk, and the slowest workgroup sets the kernel's time.)
   f32x16_t acc[8];
   float m_ref = -INFINITY;  // log2 units, this lane's head
   float l_run = 0.f;        // this lane's share of the softmax denominator (own keys)
@@ -781,7 +791,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
           if (key_visible_bit(vis0, 4 * c + e)) mx = fmax3(mx, s0[4 * c + e] + p4[e]);
       }
       have_ref = vis0 != 0;
-      m_ref = have_ref ? partner_max(mx) * sl2 : -INFINITY;
+      m_ref = have_ref ? partner_max(mx) * sl2 + kRefShift : -INFINITY;
     }
     *(LDS_AS f32x4_t*)(xs_mine) = (f32x4_t){s0[kSend], s0[kSend + 1], s0[kSend + 2], s0[kSend + 3]};
     *(LDS_AS f32x4_t*)(xs_mine + 1024) =
@@ -886,7 +896,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
             *(LDS_AS float*)(xs + wave * 2048 + lane * 4) = mt;
             __syncthreads();
             const bool adopt = !have_ref && vis != 0;
-            m_ref = adopt ? fmax3(mt, *(const LDS_AS float*)(xs + partner * 2048 + lane * 4)) : m_ref;
+            m_ref = adopt ? fmax3(mt, *(const LDS_AS float*)(xs + partner * 2048 + lane * 4)) + kRefShift : m_ref;
             have_ref = have_ref || adopt;
           }
           ovf |= mt > m_ref + kRefHeadroom;

@@ -105,3 +105,16 @@ def test_paged_entries_outside_the_pool_read_zero_rows():
     for kernel in (0, 1):
         out, lse = run_paged(case, pg, kv_index=idx, kernel=kernel)
         assert_parity(out, lse, ro, rl, f"out-of-pool entries, kernel {kernel}")
+
+
+@pytest.mark.parametrize("q,heads,p,tree", [(9, 8, 700, "random"), (5, 3, 300, "star"), (9, 128, 500, "random"),
+                                            (33, 16, 1500, "bounded")])
+def test_paged_head_counts(q, heads, p, tree):
+    """Row blocks that several tokens share, or that pad past the last
+    (token, head) row: the query block of each row block is read from rows
+    that exist only, the padded rows read as zeros and are never stored."""
+    case = gen.make_case(q, p, tree=tree, seed=4000 + q + p + heads, num_heads=heads)
+    pg = gen.make_paged(case, seed=4100 + heads, extra_rows=300)
+    out, lse = run_paged(case, pg)
+    ro, rl = oracle_paged(case, pg)
+    assert_parity(out, lse, ro, rl, f"paged H{heads} q{q} p{p}")

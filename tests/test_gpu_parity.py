@@ -182,8 +182,9 @@ def test_bad_offsets_give_nan_not_fault():
 # numerically special inputs
 # ---------------------------------------------------------------------------
 def test_reference_max_restart():
-    """A late key whose score is far above the first tile's max (beyond 2^64
-    in weight) takes the redo-the-chunk path; the result stays exact."""
+    """A late key whose score is far above the first tile's max (about 400 in
+    log2 units: its weight overflows fp32) takes the redo-the-chunk path; the
+    result stays exact."""
     case = gen.make_case(3, 200, tree="chain", seed=31, num_heads=64)
     case.kv_latent[150] = (case.q_nope[0, 0].float() * 0.5).to(torch.bfloat16)
     case.k_rope[150] = (case.q_rope[0, 0].float() * 0.5).to(torch.bfloat16)
@@ -191,6 +192,21 @@ def test_reference_max_restart():
     out, lse = run(case)
     ro, rl = oracle(case)
     assert_parity(out, lse, ro, rl, "restart")
+
+
+def test_large_weights_without_restart():
+    """A late key about 100 (log2 units) above the first tile's max: its
+    weight 2^100 is still finite in fp32, so the chunk runs once, and the
+    result (that row is nearly one-hot on the late key) stays exact."""
+    case = gen.make_case(3, 200, tree="chain", seed=32, num_heads=64)
+    q0 = torch.cat([case.q_nope[0, 0].float(), case.q_rope[0, 0].float()])
+    case.scale = 0.25
+    c = 81.0 / (case.scale * float(q0 @ q0))  # score of row (0, 0) on key 150: about 81 natural
+    case.kv_latent[150] = (case.q_nope[0, 0].float() * c).to(torch.bfloat16)
+    case.k_rope[150] = (case.q_rope[0, 0].float() * c).to(torch.bfloat16)
+    out, lse = run(case)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, "weights near 2^100")
 
 
 def test_peaky_single_key_dominates():
