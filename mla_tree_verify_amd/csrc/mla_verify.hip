@@ -9,37 +9,38 @@
 // one KV tile in shared memory serves several heads). The execution layout is
 // designed for CDNA4 rather than taken from the pages' sm_120 kernels:
 //
-//  * One workgroup = one draft token x all 64 heads x one KV chunk. Because the
-//    latent KV is shared by every head, scores and values are dense
-//    contractions: S^T[keys x heads] = K[keys x 576] Q^T and
-//    O^T[dims x heads] += V^T[dims x keys] P^T, both on bf16 MFMA 32x32x16
-//    with fp32 accumulation.
-//  * 4 waves = 2 head halves x 2 dim halves. A wave keeps the queries of its
-//    32 heads over its half of the 576 dims in registers (72 VGPRs) and
-//    computes partial scores for every 32-key tile; the two waves of a head
-//    half swap partials through LDS, so both hold the same full scores, the
-//    same softmax weights and denominators. Each then accumulates 256 of the
-//    512 output dims (128 AGPRs). Every wave reads a tile's K and V once, so a
-//    CU does about 32 MFMA flops per LDS byte.
-//  * KV tiles go from HBM straight into LDS with 16-byte buffer loads
-//    (buffer_load_dwordx4 ... lds) into a 3-slot ring; loads past the sequence
+//  * One workgroup = one row block (64 consecutive (token, head) rows of the
+//    [q, H] layout) x one KV chunk. Because the latent KV is shared by every
+//    head, scores and values are dense contractions: S^T[keys x rows] =
+//    K[keys x 576] Q^T and O^T[dims x rows] += V^T[dims x keys] P^T, both on
+//    bf16 MFMA 32x32x16 with fp32 accumulation.
+//  * 4 waves = 2 row halves x 2 dim halves, one wave per SIMD. A wave keeps
+//    the queries of its 32 rows over its half of the 576 dims in registers
+//    (72 VGPRs) and computes partial scores for every 32-key tile; each wave
+//    owns half of a tile's keys, receives the partner's partial scores of
+//    them through LDS, turns the full scores into weights, and the two waves
+//    swap weights. Each then accumulates 256 of the 512 output dims of its
+//    rows (128 AGPRs).
+//  * KV tiles (and the block's query rows, once) go from HBM straight into
+//    LDS with 16-byte buffer loads (buffer_load_dwordx4 ... lds) into a
+//    4-slot ring loaded three tiles ahead; loads past the chunk or sequence
 //    end return zeros. 16-byte chunks are XOR swizzled per key so that the
 //    128-bit score-operand reads and the transposing value-operand reads
-//    (ds_read_b64_tr_b16) avoid bank conflicts.
+//    (ds_read_b64_tr_b16) avoid most bank conflicts.
 //  * The S^T accumulator layout equals the P^T operand layout of the value
-//    product, so softmax weights never leave registers. Row max and sum need a
-//    single cross-lane step (v_permlane32_swap). The next tile's score MFMAs
-//    are issued before this tile's softmax so the two overlap.
+//    product, so softmax weights leave registers only for the swap. The next
+//    tile's score MFMAs are issued before this tile's softmax so the two
+//    overlap.
 //  * The softmax reference max is fixed by the first visible tile and never
-//    moves, so the accumulator is never rescaled inside the loop (a chunk
-//    whose scores climb more than 2^64 above it is redone once with the
-//    chunk's own max).
+//    moves, so the accumulator is never rescaled inside the loop (weights may
+//    reach 2^96; a chunk whose scores climb beyond that is redone once with
+//    the chunk's own max).
 //  * Softmax weights enter the value product as a bf16 hi+lo pair (two MFMAs
 //    sharing the V operand), about 16 significant bits; a single bf16 weight
 //    is an option.
-//  * Workgroup ids are mapped so that all tokens of one KV chunk run on the
-//    same XCD (ids are dealt round-robin over the 8 XCDs), and the chunk is
-//    read from HBM once into that XCD's L2.
+//  * Workgroup ids are mapped so that all row blocks of one KV chunk run on
+//    the same XCD (ids are dealt round-robin over the 8 XCDs), and the chunk
+//    is read from HBM once into that XCD's L2.
 
 #include <hip/hip_runtime.h>
 
@@ -69,6 +70,8 @@ constexpr int kThreads = 256;
 static_assert(kRing * 128 == kDl && 128 * 4 * kRows <= kTileBytes,
               "the epilogue stages 128 output dims of all 64 rows in each ring slot");
 static_assert(kLdsBytes <= 163840, "LDS per workgroup");
+static_assert(32 * (kDl + kDr) * 2 == kTileBytes, "32 query rows fill one ring slot in the tile layout");
+static_assert(32 * kDl * 2 <= kTileBytes, "the int16 epilogue stages 32 rows per ring slot");
 constexpr int kXcds = 8;
 constexpr int64_t kChunkGran = kTile;
 constexpr int64_t kMinChunk = 128;
@@ -570,17 +573,14 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   const int ntiles = (c1 - c0 + kTile - 1) / kTile;
   // This lane's row: row `head` of the block, (token, head) row r of the
   // sequence, r = token * heads + head index; rows past q * heads pad the last
-  // block (they repeat the last row and are never stored).
+  // block (their queries read as zeros; they take the last row's token for
+  // the tree mask, and their results are never stored as outputs).
   const int head = 32 * hh + (lane & 31);
   const int rows_seq = a.q * a.heads;
   const int r_lane = rbk * kRows + head;
   const int r_src = r_lane < rows_seq ? r_lane : rows_seq - 1;
   const int tok = r_src / a.heads;
 
-  // Tile 0 is requested before anything else, then the queries and the
-  // tree, then tiles 1 and 2, so that load latency overlaps the ancestor
-  // walk and the wait before the first scores covers tile 0 and the queries
-  // only (loads complete in issue order).
   // contiguous KV: descriptors over this chunk's rows onward; paged KV: over the pool
   const __amdgpu_buffer_rsrc_t lat_rs =
       kPaged ? make_rsrc(a.lat, (uint32_t)a.pool_rows * (kDl * 2))
