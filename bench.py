@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -61,7 +62,14 @@ def parse():
 
 
 def source_digest() -> str:
-    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source without comments and blank space, so
+    that counters stay attached to the code they were taken on across
+    comment-only edits."""
+    text = open(SRC, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def read_counters(workload: str, paged: bool = False):

@@ -338,6 +338,16 @@ def test_head_counts(heads, q, p, tree, nsplit):
     assert_parity(out, lse, ro, rl, f"H={heads} q={q} p={p}")
 
 
+@pytest.mark.parametrize("q,p,nsplit", [(64, 40, 0), (9, 3000, 4)])
+def test_max_head_count(q, p, nsplit):
+    """MLAV_MAX_HEADS = 1024 heads: 64 x 1024 = 65 536 rows in 1024 row blocks
+    (one split each), and 9 x 1024 rows over 4 forced splits (576 workgroups)."""
+    case = gen.make_case(q, p, tree="random", num_heads=1024, seed=4500 + q + p)
+    out, lse = run(case, nsplit=nsplit)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, f"H1024 q{q} p{p}")
+
+
 @pytest.mark.parametrize("heads", [8, 128])
 def test_head_counts_valu_kernel(heads):
     case = gen.make_case(9, 700, tree="random", num_heads=heads, seed=4100 + heads)
