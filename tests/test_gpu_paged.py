@@ -118,3 +118,17 @@ def test_paged_head_counts(q, heads, p, tree):
     out, lse = run_paged(case, pg)
     ro, rl = oracle_paged(case, pg)
     assert_parity(out, lse, ro, rl, f"paged H{heads} q{q} p{p}")
+
+
+def test_paged_reference_max_restart():
+    """The redo of a chunk after a weight overflow (a late key far above the
+    first tile's max) reloads its first tiles through the page table."""
+    case = gen.make_case(3, 200, tree="chain", seed=31, num_heads=64)
+    case.kv_latent[150] = (case.q_nope[0, 0].float() * 0.5).to(torch.bfloat16)
+    case.k_rope[150] = (case.q_rope[0, 0].float() * 0.5).to(torch.bfloat16)
+    case.scale = 1.0
+    pg = gen.make_paged(case, seed=33, extra_rows=100)
+    for kw in ({}, {"nsplit": 3}):
+        out, lse = run_paged(case, pg, **kw)
+        ro, rl = oracle_paged(case, pg)
+        assert_parity(out, lse, ro, rl, f"paged restart {kw}")

@@ -189,9 +189,10 @@ def test_reference_max_restart():
     case.kv_latent[150] = (case.q_nope[0, 0].float() * 0.5).to(torch.bfloat16)
     case.k_rope[150] = (case.q_rope[0, 0].float() * 0.5).to(torch.bfloat16)
     case.scale = 1.0
-    out, lse = run(case)
     ro, rl = oracle(case)
-    assert_parity(out, lse, ro, rl, "restart")
+    for kw in ({}, {"nsplit": 3}, {"nsplit": 3, "merge": 1}):
+        out, lse = run(case, **kw)
+        assert_parity(out, lse, ro, rl, f"restart {kw}")
 
 
 def test_large_weights_without_restart():
