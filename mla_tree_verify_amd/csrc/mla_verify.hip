@@ -1280,10 +1280,20 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(Args a) {
   }
 }
 
+// Every argument a combine kernel uses, in one round of scalar loads
+// (fetched lazily they took three dependent rounds, each a memory round trip
+// at kernel start).
+__device__ inline void fetch_combine_args(const Args& a, int64_t rows) {
+  asm volatile("" ::"s"(rows), "s"(a.q), "s"(a.heads), "s"(a.nrb), "s"(a.nsplit), "s"(a.chunk), "s"(a.offs),
+               "s"(a.single_n), "s"(a.total_kv), "s"(a.max_kv), "s"(a.part_q), "s"(a.part_o), "s"(a.part_lse),
+               "s"(a.part_scale), "s"(a.out), "s"(a.lse), "s"(a.fixed_ns));
+}
+
 // ---------------------------------------------------------------------------
 // combine: log-sum-exp merge of the split partials, 128 threads per row
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows) {
+  fetch_combine_args(a, rows);
   const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
   if (row >= rows) return;
   const int d4 = threadIdx.x & 127;
@@ -1352,6 +1362,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
 // fetch the lse and scale values, the max and weight sum come from 32-lane
 // reductions, and each split's weight * scale reaches all lanes by readlane.
 __global__ __launch_bounds__(64) void combine_compact_kernel(Args a, int64_t rows) {
+  fetch_combine_args(a, rows);
   const int64_t row = blockIdx.x;
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
@@ -1418,6 +1429,7 @@ __global__ __launch_bounds__(64) void combine_compact_kernel(Args a, int64_t row
 // reductions, each split's weight * scale reaches all lanes by readlane, and
 // batches are merged with a running max, as in the fp32 combine.
 __global__ __launch_bounds__(kThreads) void combine_compact_wide_kernel(Args a, int64_t rows) {
+  fetch_combine_args(a, rows);
   __shared__ float x_acc[4][kDl];
   __shared__ float x_m[4], x_w[4];
   const int64_t row = blockIdx.x;
