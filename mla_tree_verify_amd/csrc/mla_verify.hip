@@ -221,6 +221,16 @@ __device__ inline int swz_rope(int k) { return (k >> 1) & 7; }
 
 __device__ inline float fmax3(float a, float b) { return __builtin_fmaxf(a, b); }
 
+// max(m, |a|, |b|) in one v_max3_f32 with abs modifiers. Written out because
+// for values read from accumulator registers the compiler emitted two-input
+// maxes plus canonicalising moves (about 3.6 instructions per value instead
+// of 0.5).
+__device__ inline float max3_abs(float m, float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
 __device__ inline float partner_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmax3(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -1064,7 +1074,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int e = 0; e < 16; e += 2)
-        mx[(e >> 1) & 3] = fmax3(mx[(e >> 1) & 3], fmax3(__builtin_fabsf(acc[db][e]), __builtin_fabsf(acc[db][e + 1])));
+        mx[(e >> 1) & 3] = max3_abs(mx[(e >> 1) & 3], acc[db][e], acc[db][e + 1]);
     float m = partner_max(fmax3(fmax3(mx[0], mx[1]), fmax3(mx[2], mx[3])));
     *(LDS_AS float*)(xs + wave * 2048 + 1024 + lane * 4) = m;  // clear of the l_tot words read above
     __syncthreads();
