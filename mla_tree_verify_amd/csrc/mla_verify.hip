@@ -1368,9 +1368,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
 // row, one row per workgroup (the rows spread over every CU; at short
 // prefixes this launch is latency-bound, and four-wave workgroups left half
 // the CUs idle); lane l owns dims [8 l, 8 l + 8), one 16-byte load per split, and all
-// loads of a row are in flight together (one memory round trip). Lanes 0..31
-// fetch the lse and scale values, the max and weight sum come from 32-lane
-// reductions, and each split's weight * scale reaches all lanes by readlane.
+// loads of a row are in flight together (one memory round trip; kBatch loads
+// per lane, the plan's split count rounded up to a power of two, at least 4).
+// Lanes 0..31 fetch the lse and scale values, the max and weight sum come
+// from 32-lane reductions, and each split's weight * scale reaches all lanes
+// by readlane.
+template <int kBatch>
 __global__ __launch_bounds__(64) void combine_compact_kernel(Args a, int64_t rows) {
   fetch_combine_args(a, rows);
   const int64_t row = blockIdx.x;
@@ -1394,7 +1397,6 @@ __global__ __launch_bounds__(64) void combine_compact_kernel(Args a, int64_t row
   const float* pl = a.part_lse + base;
   const float* psc = a.part_scale + base;
   const int16_t* pq = a.part_q + base * kDl + 8 * lane;
-  constexpr int kBatch = 32;
   u32x4_t qv[kBatch];
 #pragma unroll
   for (int k = 0; k < kBatch; ++k) {
@@ -1703,10 +1705,17 @@ merge:
   if (p.combine == 1) {
     const int64_t rows = (int64_t)a.batch * a.q * a.heads;
     if (compact) {
-      if (p.nsplit <= 32)
-        hipLaunchKernelGGL(combine_compact_kernel, dim3((unsigned)rows), dim3(64), 0, st, a, rows);
-      else
+      if (p.nsplit <= 32) {
+        // loads per lane: the plan's split count rounded up to a power of two
+        using C = void (*)(Args, int64_t);
+        const C k = p.nsplit <= 4 ? combine_compact_kernel<4>
+                    : p.nsplit <= 8 ? combine_compact_kernel<8>
+                    : p.nsplit <= 16 ? combine_compact_kernel<16>
+                                     : combine_compact_kernel<32>;
+        hipLaunchKernelGGL(k, dim3((unsigned)rows), dim3(64), 0, st, a, rows);
+      } else {
         hipLaunchKernelGGL(combine_compact_wide_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, rows);
+      }
     } else {
       hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
     }
