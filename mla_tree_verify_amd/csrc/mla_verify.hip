@@ -1369,7 +1369,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
 // prefixes this launch is latency-bound, and four-wave workgroups left half
 // the CUs idle); lane l owns dims [8 l, 8 l + 8), one 16-byte load per split, and all
 // loads of a row are in flight together (one memory round trip; kBatch loads
-// per lane, the plan's split count rounded up to a power of two, at least 4).
+// per lane, the plan's split count rounded up to a multiple of 4).
 // Lanes 0..31 fetch the lse and scale values, the max and weight sum come
 // from 32-lane reductions, and each split's weight * scale reaches all lanes
 // by readlane.
@@ -1706,13 +1706,13 @@ merge:
     const int64_t rows = (int64_t)a.batch * a.q * a.heads;
     if (compact) {
       if (p.nsplit <= 32) {
-        // loads per lane: the plan's split count rounded up to a power of two
+        // loads per lane: the plan's split count rounded up to a multiple of 4
         using C = void (*)(Args, int64_t);
-        const C k = p.nsplit <= 4 ? combine_compact_kernel<4>
-                    : p.nsplit <= 8 ? combine_compact_kernel<8>
-                    : p.nsplit <= 16 ? combine_compact_kernel<16>
-                                     : combine_compact_kernel<32>;
-        hipLaunchKernelGGL(k, dim3((unsigned)rows), dim3(64), 0, st, a, rows);
+        static const C by_batch[8] = {combine_compact_kernel<4>,  combine_compact_kernel<8>,
+                                      combine_compact_kernel<12>, combine_compact_kernel<16>,
+                                      combine_compact_kernel<20>, combine_compact_kernel<24>,
+                                      combine_compact_kernel<28>, combine_compact_kernel<32>};
+        hipLaunchKernelGGL(by_batch[(p.nsplit + 3) / 4 - 1], dim3((unsigned)rows), dim3(64), 0, st, a, rows);
       } else {
         hipLaunchKernelGGL(combine_compact_wide_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, rows);
       }
