@@ -1053,8 +1053,8 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   const int64_t out_row0 = (int64_t)b * rows_seq + rbk * kRows;  // first output row of the block
   const int nvalid = rows_seq - rbk * kRows < kRows ? rows_seq - rbk * kRows : kRows;
   const int64_t prow = (((int64_t)b * a.nsplit + s) * a.nrb + rbk) * kRows;  // first partial row
-  // Partials keep the padded row block (all 64 rows); the final output takes
-  // the block's rows below q * heads only.
+  // fp32 partials keep the padded row block (all 64 rows); int16 partials and
+  // the final output take the block's rows below q * heads only.
   if (compact) {
     // Compact partials: row h of the normalised partial is stored as 512
     // int16 values q with one fp32 scale, value = q * scale, where scale =
@@ -1113,11 +1113,15 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     __syncthreads();
     const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.part_q + prow * kDl, kRows * kDl * 2);
     LDS_AS char* src = ring(wave >> 1);  // rows 16 wave .. 16 wave + 15 lie in slot wave >> 1
+    // Rows past q * heads (the padding of the last block) are not stored: no
+    // merge writes them, and each row merges on its own.
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int h = 16 * wave + k;
-      const u32x4_t v = *(const LDS_AS u32x4_t*)(src + (h & 31) * 1024 + 16 * (lane ^ (h & 31)));
-      __builtin_amdgcn_raw_buffer_store_b128(v, prs, h * (kDl * 2) + 16 * lane, 0, kCoherent);
+      if (h < nvalid) {
+        const u32x4_t v = *(const LDS_AS u32x4_t*)(src + (h & 31) * 1024 + 16 * (lane ^ (h & 31)));
+        __builtin_amdgcn_raw_buffer_store_b128(v, prs, h * (kDl * 2) + 16 * lane, 0, kCoherent);
+      }
     }
   } else {
     // Stage the accumulators through LDS so that each global store writes
