@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--rotate-mb", type=float, default=768.0, help="bytes of rotating input copies (cold run)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target host time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
                     help="after timing, run one device copy of this size (counter calibration)")
     ap.add_argument("--pv-mode", type=int, default=0)
@@ -244,6 +245,45 @@ def main() -> int:
     split_us = batch_us(split)
     combine_us = batch_us(merge) if plan.combine == 1 else 0.0
 
+    # The whole call replayed from a HIP graph, as a serving loop would issue
+    # it: one graph makes the call on every input copy in turn (cold, like
+    # us_cold). Inside the capture the launches go to the capture stream, so
+    # the arguments carry that stream. The replayed output must equal the
+    # eager output bit for bit (the kernels are deterministic).
+    graph_us = graph_equal = None
+    if not args.no_graph:
+        d0 = copies[0]
+        call(d0)
+        torch.cuda.synchronize()
+        eager = (d0["out"].clone(), d0["lse"].clone())
+        d0["out"].zero_()
+        d0["lse"].zero_()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        with torch.cuda.graph(g, stream=cap):
+            for d in copies:
+                a = list(d["args"][0])
+                a[-2] = cap.cuda_stream
+                rc = entry(*a)
+                if rc != _lib.MLAV_OK:
+                    raise _lib.MLAVError(rc, "verify call under graph capture")
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < 100.0:
+            g.replay()
+            torch.cuda.synchronize()
+        reps = max(1, args.steps // ncopy)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / (reps * ncopy)
+        graph_equal = bool(torch.equal(d0["out"], eager[0]) and torch.equal(d0["lse"], eager[1]))
+        del g
+
     if args.copy_calib_mb > 0:
         nb = int(args.copy_calib_mb * 2**20) // 4 * 4
         src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -307,6 +347,8 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "us_per_call": round(us_cold, 2),
         "us_per_call_warm": round(us_warm, 2),
+        "us_per_call_graph": None if graph_us is None else round(graph_us, 2),
+        "graph_replay_equals_eager": graph_equal,
         "tflops_warm": round(tflops_warm, 2),
         "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(alg_bytes / (us_cold * 1e-6) / 1e9, 1),
