@@ -116,7 +116,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the verify operator has no "
-                          "multi-GPU path here (see the sharding notes in DESIGN.md)",
+                          "multi-GPU path: sharded, each GPU would run the same call on its own heads or "
+                          "sequences with no communication",
                           "n_gpus": args.gpus}))
         return 2
 
