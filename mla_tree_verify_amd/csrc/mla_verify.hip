@@ -1439,11 +1439,13 @@ __global__ __launch_bounds__(64) void combine_compact_kernel(Args a, int64_t row
 // Combine of compact (int16 + scale) partials for more than 32 splits: one
 // workgroup per row; wave w merges splits [w ns / 4, (w + 1) ns / 4) and the
 // four partial merges meet in LDS. Lane l owns dims [8 l, 8 l + 8), one 16-byte load per split. A
-// wave takes its splits in batches of 32 (one memory round trip each): every
+// wave takes its splits in batches of kBatch (its share of the plan's splits
+// rounded up to a multiple of 4, at most 32; one memory round trip each): every
 // partial load of a batch is issued first, lanes 0..31 fetch the batch's lse
 // and scale values, the batch max and weight sum come from 32-lane
 // reductions, each split's weight * scale reaches all lanes by readlane, and
 // batches are merged with a running max, as in the fp32 combine.
+template <int kBatch>
 __global__ __launch_bounds__(kThreads) void combine_compact_wide_kernel(Args a, int64_t rows) {
   fetch_combine_args(a, rows);
   __shared__ float x_acc[4][kDl];
@@ -1473,7 +1475,6 @@ __global__ __launch_bounds__(kThreads) void combine_compact_wide_kernel(Args a, 
   const float* psc = a.part_scale + base;
   const int16_t* pq = a.part_q + base * kDl + 8 * lane;
   const int s_lo = wave * ns / 4, s_hi = (wave + 1) * ns / 4;
-  constexpr int kBatch = 32;
   float M = -INFINITY, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = s_lo; s0 < s_hi; s0 += kBatch) {
@@ -1718,7 +1719,14 @@ merge:
                                       combine_compact_kernel<28>, combine_compact_kernel<32>};
         hipLaunchKernelGGL(by_batch[(p.nsplit + 3) / 4 - 1], dim3((unsigned)rows), dim3(64), 0, st, a, rows);
       } else {
-        hipLaunchKernelGGL(combine_compact_wide_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, rows);
+        // loads per lane and batch: a wave's share of the splits, rounded up to a multiple of 4
+        using C = void (*)(Args, int64_t);
+        static const C by_batch[6] = {combine_compact_wide_kernel<12>, combine_compact_wide_kernel<16>,
+                                      combine_compact_wide_kernel<20>, combine_compact_wide_kernel<24>,
+                                      combine_compact_wide_kernel<28>, combine_compact_wide_kernel<32>};
+        const int per_wave = (p.nsplit + 3) / 4;  // at least 9 here
+        hipLaunchKernelGGL(by_batch[per_wave > 32 ? 5 : (per_wave + 3) / 4 - 3], dim3((unsigned)rows),
+                           dim3(kThreads), 0, st, a, rows);
       }
     } else {
       hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);

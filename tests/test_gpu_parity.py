@@ -380,6 +380,19 @@ def test_head_counts_partials_padded_rows():
     assert torch.equal(o2.cpu()[:72].view_as(out), out) and torch.equal(l2.cpu()[:72].view_as(lse), lse)
 
 
+@pytest.mark.parametrize("prefix,nsplit", [(4727, 74), (6391, 100), (4471, 140), (6007, 188)])
+def test_wide_combine_batch_sizes(prefix, nsplit):
+    """The four-wave combine at split counts whose per-wave share needs 20 and
+    28 loads per lane, and past 128 splits (batches of 32 merged with a
+    running max), against the oracle."""
+    case = gen.make_case(9, prefix, tree="random", seed=4500 + nsplit)
+    pl = api.device_plan(9, 1, prefix + 9, prefix + 9, nsplit=nsplit)
+    assert pl.nsplit == nsplit
+    out, lse = run(case, nsplit=nsplit)
+    ro, rl = oracle(case)
+    assert_parity(out, lse, ro, rl, f"compact, {pl.nsplit} splits")
+
+
 @pytest.mark.parametrize("nsplit", [5, 32, 33, 40, 100])
 def test_compact_combine_split_counts(nsplit):
     """Both combine forms of the int16 partials (one wave per row up to 32
