@@ -380,6 +380,31 @@ def test_head_counts_partials_padded_rows():
     assert torch.equal(o2.cpu()[:72].view_as(out), out) and torch.equal(l2.cpu()[:72].view_as(lse), lse)
 
 
+@pytest.mark.parametrize("heads,prefix,nsplit", [(8, 6000, 0), (8, 3000, 20)])
+def test_padding_rows_of_int16_partials_are_never_read(heads, prefix, nsplit):
+    """q * H = 72 rows: the last row block is mostly padding, whose int16
+    partial rows the split kernel does not store. A workspace of random bytes
+    must give the bitwise result of a zeroed one (four-wave combine for the
+    planner's 47 splits at prefix 6000, one-wave combine for 19 splits at
+    prefix 3000), which also matches the oracle."""
+    case = gen.make_case(9, prefix, tree="random", num_heads=heads, seed=4600 + nsplit)
+    d = dev_case(case)
+    n = prefix + 9
+    pl = api.device_plan(9, 1, n, n, nsplit=nsplit, num_heads=heads)
+    assert pl.nsplit == (47 if nsplit == 0 else 19)
+    need = _lib.workspace_size(9, heads, 1, n, n, nsplit=nsplit)
+    assert need > 0
+    args = (d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], prefix, case.scale)
+    o0, l0 = api.mla_verify(*args, workspace=torch.zeros(need, dtype=torch.uint8, device=DEV), nsplit=nsplit)
+    g = torch.Generator().manual_seed(11)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=g).to(DEV)
+    o1, l1 = api.mla_verify(*args, workspace=ws, nsplit=nsplit)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    ro, rl = oracle(case)
+    assert_parity(o1.cpu(), l1.cpu(), ro, rl, f"H {heads}, padded rows, nsplit {nsplit}")
+
+
 @pytest.mark.parametrize("prefix,nsplit", [(4727, 74), (6391, 100), (4471, 140), (6007, 188)])
 def test_wide_combine_batch_sizes(prefix, nsplit):
     """The four-wave combine at split counts whose per-wave share needs 20 and
