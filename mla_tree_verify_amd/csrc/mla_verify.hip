@@ -74,7 +74,11 @@ static_assert(32 * (kDl + kDr) * 2 == kTileBytes, "32 query rows fill one ring s
 static_assert(32 * kDl * 2 <= kTileBytes, "the int16 epilogue stages 32 rows per ring slot");
 constexpr int kXcds = 8;
 constexpr int64_t kChunkGran = kTile;
-constexpr int64_t kMinChunk = 128;
+// Smallest chunk the planner picks by itself: two tiles. Below that the
+// per-workgroup fixed cost outweighs the extra CUs (at prefix 256, q 9:
+// 64-key chunks 13.5 us per call, 32-key 13.4 us, 128-key 15.1 us; at
+// prefix 512 64-key chunks beat 32-key ones).
+constexpr int64_t kMinChunk = 64;
 // Reference max placement, log2 units: the reference sits kRefShift above
 // the first tile's max, so that tile's largest weight is 2^-32 and weights
 // may grow to 2^96 (scores up to 128 above that max) before a redo; keys more

@@ -98,7 +98,7 @@ def test_plan_merged_in_split_kernel(lib):
     split kernel (combine = 2) and add one 8-byte ticket per row block to the
     workspace; merge = 0 (the default), fp32 partials or the VALU kernel keep
     the combine kernel."""
-    for n, ns in [(200, 2), (300, 3), (500, 4)]:
+    for n, ns in [(100, 2), (150, 3), (250, 4)]:
         pl = _lib.plan(9, 64, 1, n, n, 256, merge=1)
         assert pl.nsplit == ns and pl.combine == 2
         ws = _lib.workspace_size(9, 64, 1, n, n, num_cus=256, merge=1)
@@ -109,15 +109,15 @@ def test_plan_merged_in_split_kernel(lib):
         assert _lib.plan(9, 64, 1, n, n, 256, partials=1, merge=1).combine == 1
         assert _lib.plan(9, 64, 1, n, n, 256, kernel=1, merge=1).combine == 1
     # 5 or more splits: the combine kernel
-    pl5 = _lib.plan(9, 64, 1, 600, 600, 256, merge=1)
+    pl5 = _lib.plan(9, 64, 1, 300, 300, 256, merge=1)
     assert pl5.nsplit == 5 and pl5.combine == 1
     # batched, any head count: tickets for every (sequence, row block)
-    pl = _lib.plan(9, 8, 3, 3 * 300, 300, 256, merge=1)
+    pl = _lib.plan(9, 8, 3, 3 * 150, 150, 256, merge=1)
     assert pl.combine == 2
-    assert (_lib.workspace_size(9, 8, 3, 900, 300, num_cus=256, merge=1)
+    assert (_lib.workspace_size(9, 8, 3, 450, 150, num_cus=256, merge=1)
             == 3 * pl.nsplit * 2 * 64 * (512 * 2 + 8) + 3 * 2 * 8)
     # one split: no workspace, no combine
-    assert _lib.plan(9, 64, 1, 100, 100, 256, merge=1).combine == 0
+    assert _lib.plan(9, 64, 1, 60, 60, 256, merge=1).combine == 0
 
 
 def test_plan_errors(lib):
@@ -231,4 +231,4 @@ def test_plan_counts_row_blocks(lib):
     for heads, blocks in ((64, 9), (8, 2), (16, 3), (128, 18), (1, 1)):
         pl = _lib.plan(9, heads, 1, n, n, 256)
         assert pl.grid >= blocks * pl.nsplit and pl.grid % 8 == 0
-        assert blocks * pl.nsplit <= 256 or pl.chunk == 128
+        assert blocks * pl.nsplit <= 256 or pl.chunk == 64

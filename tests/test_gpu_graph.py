@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("prefix,nsplit,merge", [(16384, 0, 0), (256, 0, 0), (256, 0, 1), (300, 1, 0)])
+@pytest.mark.parametrize("prefix,nsplit,merge", [(16384, 0, 0), (256, 0, 0), (150, 0, 1), (300, 1, 0)])
 def test_graph_replays_match_eager(prefix, nsplit, merge):
     """merge = 1 at prefix 256: the split kernel merges its 3 splits (tickets
     in the workspace, reset by the last workgroup, same epoch on every replay)."""

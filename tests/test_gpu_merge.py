@@ -45,9 +45,9 @@ def run(case: gen.Case, **kw):
 
 
 # (q, heads, prefix, tree): 2, 3 and 4 splits, head counts below, at and above 64
-CASES = [(9, 64, 150, "random"), (9, 64, 256, "random"), (9, 64, 500, "bounded"), (1, 64, 200, "random"),
-         (33, 64, 300, "random"), (64, 64, 400, "random"), (9, 8, 300, "random"), (9, 16, 400, "chain"),
-         (9, 128, 256, "random"), (5, 3, 300, "star")]
+CASES = [(9, 64, 150, "random"), (9, 64, 100, "random"), (9, 64, 220, "bounded"), (1, 64, 200, "random"),
+         (33, 64, 150, "random"), (64, 64, 400, "random"), (9, 8, 180, "random"), (9, 16, 240, "chain"),
+         (9, 128, 120, "random"), (5, 3, 150, "star")]
 
 
 @pytest.mark.parametrize("q,heads,p,tree", CASES)
@@ -75,19 +75,19 @@ def test_merged_equals_combine_kernel(q, heads, p, tree):
 def test_merged_on_garbage_workspace_and_tickets_reset():
     """The ticket words need no clearing: a workspace of random bytes gives
     the bitwise result of a zeroed one, and every ticket is 0 after the call."""
-    case = gen.make_case(9, 300, tree="random", seed=7200)
-    n = 309
+    case = gen.make_case(9, 150, tree="random", seed=7200)
+    n = 159
     need = _lib.workspace_size(9, 64, 1, n, n, merge=1)
     tickets = 9 * 8  # one 8-byte word per row block, at the end of the workspace
     qn, qr, lat, rope, par = dev_inputs(case)
     ws0 = torch.zeros(need, dtype=torch.uint8, device=DEV)
-    o0, l0 = api.mla_verify(qn, qr, lat, rope, par, 300, case.scale, workspace=ws0, merge=1)
+    o0, l0 = api.mla_verify(qn, qr, lat, rope, par, 150, case.scale, workspace=ws0, merge=1)
     g = torch.Generator().manual_seed(1)
     for k in range(3):
         ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=g).to(DEV)
         if k == 2:  # every word a ticket of some other epoch with a count of 1
             ws[-tickets:].view(torch.int64).fill_((12345 << 16) | 1)
-        o, l = api.mla_verify(qn, qr, lat, rope, par, 300, case.scale, workspace=ws, merge=1)
+        o, l = api.mla_verify(qn, qr, lat, rope, par, 150, case.scale, workspace=ws, merge=1)
         torch.cuda.synchronize()
         assert torch.equal(o, o0) and torch.equal(l, l0), f"garbage workspace {k}"
         assert int(ws[-tickets:].count_nonzero()) == 0, "tickets not reset"
@@ -96,7 +96,7 @@ def test_merged_on_garbage_workspace_and_tickets_reset():
 def test_merged_batched_mixed_split_counts():
     """Sequences of 1, 2, 3 and 4 splits in one call: one-split sequences
     write directly, the others merge in the kernel."""
-    lens = [50, 200, 300, 450]
+    lens = [30, 80, 150, 220]
     case = gen.make_batched_case(4, 9, prefix_lens=lens, tree="random", seed=7300)
     total = int(case.kv_offsets[-1])
     pl = _lib.plan(9, 64, 4, total, max(lens) + 9, cus(), merge=1)
@@ -111,7 +111,7 @@ def test_merged_batched_mixed_split_counts():
 
 
 def test_merged_paged():
-    case = gen.make_case(9, 350, tree="random", seed=7400)
+    case = gen.make_case(9, 180, tree="random", seed=7400)
     pg = gen.make_paged(case, seed=7401, extra_rows=500)
     out, lse = api.mla_verify_paged(case.q_nope.to(DEV), case.q_rope.to(DEV), pg.pool_latent.to(DEV),
                                     pg.pool_rope.to(DEV), pg.kv_index.to(DEV), case.tree_parent.to(DEV), case.scale,
@@ -125,12 +125,12 @@ def test_merged_paged():
 def test_merged_run_to_run_bitwise():
     """Whichever workgroup arrives last, the merge reads the same partials in
     the same order: repeated calls on one workspace are bitwise equal."""
-    case = gen.make_case(33, 400, tree="random", seed=7500)
+    case = gen.make_case(33, 150, tree="random", seed=7500)
     qn, qr, lat, rope, par = dev_inputs(case)
-    ws = torch.empty(_lib.workspace_size(33, 64, 1, 433, 433, merge=1), dtype=torch.uint8, device=DEV)
-    o0, l0 = api.mla_verify(qn, qr, lat, rope, par, 400, case.scale, workspace=ws, merge=1)
+    ws = torch.empty(_lib.workspace_size(33, 64, 1, 183, 183, merge=1), dtype=torch.uint8, device=DEV)
+    o0, l0 = api.mla_verify(qn, qr, lat, rope, par, 150, case.scale, workspace=ws, merge=1)
     o0, l0 = o0.clone(), l0.clone()
     for _ in range(20):
-        o, l = api.mla_verify(qn, qr, lat, rope, par, 400, case.scale, workspace=ws, merge=1)
+        o, l = api.mla_verify(qn, qr, lat, rope, par, 150, case.scale, workspace=ws, merge=1)
         assert torch.equal(o, o0) and torch.equal(l, l0)
     torch.cuda.synchronize()
