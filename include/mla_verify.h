@@ -42,6 +42,14 @@
  *    and write NaN for a sequence whose offsets are inconsistent.
  *  - Launch failures return MLAV_ERR_HIP; faults inside a kernel surface at the
  *    caller's next synchronisation.
+ *  - Numeric range (a precondition the host cannot check without reading the
+ *    device data): every score s[i,h,j] and every partial 576-term dot product
+ *    must be finite in fp32, and |kv_latent| < 2^31 (about 2.1e9). Under these
+ *    the results are finite: inside a chunk the softmax weights stay at most
+ *    2^96 relative to a fixed reference, a chunk whose scores climb past that
+ *    or whose fp32 accumulators overflow is redone once with the chunk's own
+ *    maximum as the reference (weights at most 1), and below 2^31 no single
+ *    weight x value product overflows.
  */
 #ifndef MLA_VERIFY_H
 #define MLA_VERIFY_H
@@ -73,6 +81,7 @@ extern "C" {
                                latent rows must stay below 2^32) */
 #define MLAV_MAX_POOL 4000000 /* rows of a paged KV pool (byte offsets into the pool's
                                  latent rows must stay below 2^32) */
+#define MLAV_MAX_COMBINE_ROWS (1 << 24) /* rows of one mla_verify_combine call */
 
 /* Tuning knobs; a NULL options pointer means all zeros. */
 typedef struct mlav_options {
@@ -153,6 +162,12 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
                       const mlav_options* opt);
 
 /*
+ * Several sequences in one call: the pages' grid spans the batch as well as
+ * the query positions, head groups and KV splits (page "The Decisive
+ * Microbench", section "The KV-Split Solution"; page "The Moment of Truth",
+ * section "The Analysis: Occupancy Starvation", one block per batch entry,
+ * query position and head tile). Ragged prefixes are stored back to back with
+ * an offsets array (this library's layout; the pages benchmark one stream).
  * batch independent sequences sharing q_len; sequence b owns KV rows
  * [kv_offsets[b], kv_offsets[b+1]) (its prefix then its q_len tree tokens).
  *   q_nope_absorbed [batch, q_len, num_heads, 512], q_rope [batch, q_len, num_heads, 64]
@@ -197,14 +212,23 @@ int32_t mla_verify_paged(const void* q_nope_absorbed, const void* q_rope, const 
                          void* stream, const mlav_options* opt);
 
 /* Workspace bytes a call with these sizes and options needs (0 when no split
-   is needed); it depends on opt->partials.
+   is needed): the scratch where each KV split leaves its partial result and
+   statistics for the merge (page "The Decisive Microbench", section "The
+   KV-Split Solution"). It depends on opt->partials.
    num_cus = 0 queries the current HIP device; pass the CU count to plan
    without a device. For one sequence use batch = 1 and
    total_kv = max_kv = prefix_len + q_len. Returns 0 for invalid sizes. */
 size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
                                  int64_t max_kv, int32_t num_cus, const mlav_options* opt);
 
-/* The planner as a pure host function (no HIP call). */
+/* The planner as a pure host function (no HIP call): the split count and the
+   chunk length, chosen so that the (sequence, row block, split) work items
+   fill the GPU's CUs at short prefixes as well as long ones (page "The
+   Decisive Microbench", section "The KV-Split Solution": partitioning the KV
+   across blocks so that enough blocks exist to keep every SM busy; page "The
+   Validation Milestone", section "The Problem: Occupancy Starvation").
+   Returns MLAV_ERR_SHAPE for sizes out of range, MLAV_ERR_ARG for
+   num_cus < 1 or invalid options; plan_out is written only on MLAV_OK. */
 int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
                         int64_t max_kv, int32_t num_cus, const mlav_options* opt,
                         mlav_plan* plan_out);
@@ -225,7 +249,8 @@ int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t
  * (e.g. KV shards) can be stacked and combined the same way; a split that sees
  * no visible key has lse = -inf and a zero output. The plan must satisfy
  * nsplit = ceil((prefix_len + q_len) / chunk) with chunk a positive multiple of
- * plan->tile (32); otherwise MLAV_ERR_ARG. Other arguments as for mla_verify.
+ * plan->tile (32) and at most MLAV_MAX_KV; otherwise MLAV_ERR_ARG. Other
+ * arguments as for mla_verify.
  */
 int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
                             const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
@@ -236,9 +261,16 @@ int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, con
 /* Host-side check of a HOST copy of a tree: MLAV_OK or MLAV_ERR_TREE. */
 int32_t mla_verify_check_tree(const int32_t* host_parent, int32_t q_len);
 
-/* The combine kernel alone, on caller-made partials:
+/* The combine kernel alone, on caller-made partials: the log-sum-exp merge of
+   the split partials (page "The Decisive Microbench", section "The KV-Split
+   Solution": a light second kernel merges the per-split results using their
+   statistics).
    part_out [nsplit, rows, 512] fp32 (each normalised), part_lse [nsplit, rows]
-   fp32 (natural log; -inf marks an empty part) -> out [rows, 512], lse [rows]. */
+   fp32 (natural log; -inf marks an empty part) -> out [rows, 512], lse [rows].
+   rows must be a positive multiple of 64 (MLAV_ROWS: the padded row layout
+   mla_verify_partials writes) and at most MLAV_MAX_COMBINE_ROWS; otherwise
+   MLAV_ERR_SHAPE. nsplit >= 1. A row whose parts are all empty gets out = 0
+   and lse = -inf. */
 int32_t mla_verify_combine(const float* part_out, const float* part_lse, int32_t nsplit,
                            int64_t rows, float* out, float* lse, void* stream);
 

@@ -740,6 +740,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
   float l_run = 0.f;        // this lane's share of the softmax denominator (own keys)
   float m_seen = -INFINITY; // max over own keys
   bool have_ref = false;    // this lane's row has seen a visible key (fixed its m_ref)
+  float acc_amax = 0.f;     // largest |accumulator| of this lane after the chunk
   // A chunk that starts inside the prefix gives every row a visible key in
   // its first tile, so all rows fix m_ref there. A chunk of tree keys only
   // (rows of several tokens can see different keys) may leave rows without a
@@ -1021,6 +1022,23 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       const uint32_t vis = tile_visibility(c0 + (int64_t)i * kTile, c1, prefix, anc);
       step(std::true_type{}, ring((i + 1) & 3), ring(i & 3), ring((i + 3) & 3), i, vis);
     }
+    // Accumulator overflow: weights reach 2^96 before a redo, so values of
+    // 2^32 / (keys in the chunk) and more can push a sum past fp32. The
+    // largest |accumulator| of the lane (also the int16 quantisation's row
+    // maximum below) catches it, and the chunk is then redone with its own
+    // maximum as the reference (weights at most 1). Below 2^31 no single
+    // product overflows, so a sum that overflowed holds an infinity, which
+    // this maximum sees.
+    {
+      float mx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2)
+          mx[(e >> 1) & 3] = max3_abs(mx[(e >> 1) & 3], acc[db][e], acc[db][e + 1]);
+      acc_amax = fmax3(fmax3(mx[0], mx[1]), fmax3(mx[2], mx[3]));
+      ovf |= !(acc_amax <= 3.402823466e38f);
+    }
     // workgroup-wide OR of the overflow flags, through the exchange area
     // (every wave is past its last read of it once all pass the barrier)
     __syncthreads();
@@ -1073,13 +1091,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // dims (the lower lane takes g = 2 gp, the upper g = 2 gp + 1). Rows are
     // staged in int16 (row h in ring slot h >> 5 at (h & 31) * 1024, 16-byte
     // chunk j at 16 (j ^ (h & 31))) and leave as one 1 KB store per row.
-    float mx[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; e += 2)
-        mx[(e >> 1) & 3] = max3_abs(mx[(e >> 1) & 3], acc[db][e], acc[db][e + 1]);
-    float m = partner_max(fmax3(fmax3(mx[0], mx[1]), fmax3(mx[2], mx[3])));
+    float m = partner_max(acc_amax);
     *(LDS_AS float*)(xs + wave * 2048 + 1024 + lane * 4) = m;  // clear of the l_tot words read above
     __syncthreads();
     m = fmax3(m, *(const LDS_AS float*)(xs + partner * 2048 + 1024 + lane * 4));  // largest |acc| of the row
@@ -1773,11 +1785,15 @@ size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch
   return workspace_bytes_for(p, q_len, num_heads, batch, compact_partials(opt));
 }
 
-int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
-                      const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
-                      float scale, float* out, float* lse, int32_t q_len, int32_t num_heads,
-                      void* workspace, size_t workspace_bytes, void* stream,
-                      const mlav_options* opt) {
+}  // extern "C"
+
+namespace mlav {
+
+// One sequence: the body of mla_verify_ex.
+int verify_single(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                  const void* k_rope, const int32_t* tree_parent, int64_t prefix_len, float scale,
+                  float* out, float* lse, int32_t q_len, int32_t num_heads, void* workspace,
+                  size_t workspace_bytes, void* stream, const mlav_options* opt) {
   int rc = common_checks(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, scale, out, lse,
                          q_len, num_heads, opt);
   if (rc != MLAV_OK) return rc;
@@ -1811,6 +1827,19 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
   a.heads = num_heads;
   a.batch = 1;
   return launch(a, p, opt, stream);
+}
+
+}  // namespace mlav
+
+extern "C" {
+
+int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                      const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
+                      float scale, float* out, float* lse, int32_t q_len, int32_t num_heads,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      const mlav_options* opt) {
+  return verify_single(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, prefix_len, scale, out,
+                       lse, q_len, num_heads, workspace, workspace_bytes, stream, opt);
 }
 
 int32_t mla_verify(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
@@ -1926,8 +1955,10 @@ int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, con
   if (!plan) return MLAV_ERR_NULL;
   if (prefix_len < 0 || prefix_len + q_len > MLAV_MAX_KV) return MLAV_ERR_SHAPE;
   const int64_t n = prefix_len + q_len;
-  if (plan->tile != kTile || plan->chunk < kTile || plan->chunk % kTile != 0 || plan->nsplit < 1 ||
-      plan->nsplit != (n + plan->chunk - 1) / plan->chunk)
+  // the kernels take the chunk as a 32-bit key count: a chunk longer than any
+  // sequence is refused rather than narrowed
+  if (plan->tile != kTile || plan->chunk < kTile || plan->chunk > MLAV_MAX_KV || plan->chunk % kTile != 0 ||
+      plan->nsplit < 1 || plan->nsplit != (n + plan->chunk - 1) / plan->chunk)
     return MLAV_ERR_ARG;
   mlav_plan p = *plan;
   const int kernel = opt ? opt->kernel : 0;
@@ -1967,7 +1998,8 @@ int32_t mla_verify_check_tree(const int32_t* host_parent, int32_t q_len) {
 int32_t mla_verify_combine(const float* part_out, const float* part_lse, int32_t nsplit,
                            int64_t rows, float* out, float* lse, void* stream) {
   if (!part_out || !part_lse || !out || !lse) return MLAV_ERR_NULL;
-  if (nsplit < 1 || rows < 1 || rows > (int64_t(1) << 34)) return MLAV_ERR_SHAPE;
+  // two rows per 256-thread workgroup: rows * 128 work items must stay below 2^32
+  if (nsplit < 1 || rows < 1 || rows > MLAV_MAX_COMBINE_ROWS) return MLAV_ERR_SHAPE;
   if (!aligned(part_out, 16) || !aligned(out, 16) || !aligned(part_lse, 4) || !aligned(lse, 4))
     return MLAV_ERR_ALIGN;
   if (rows % kRows != 0) return MLAV_ERR_SHAPE;  // whole row blocks (padded partial layout)

@@ -10,5 +10,4 @@ from .mla_verify_oracle import (  # noqa: F401
     mla_verify_batched,
     to_f64,
     visible_key_count,
-    visible_rows,
 )

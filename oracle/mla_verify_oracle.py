@@ -79,16 +79,6 @@ def ancestors_inclusive(parent: Sequence[int]) -> List[List[int]]:
     return out
 
 
-def visible_rows(parent: Sequence[int], prefix_len: int) -> List[np.ndarray]:
-    """Key rows visible to each draft token: the whole prefix [0, P) plus
-    row P + t for every t in anc*(i) (tree node t is stored at row P + t)."""
-    rows = []
-    for anc in ancestors_inclusive(parent):
-        rows.append(np.concatenate([np.arange(prefix_len, dtype=np.int64),
-                                    prefix_len + np.asarray(anc, dtype=np.int64)]))
-    return rows
-
-
 # --------------------------------------------------------------------------
 # attention over an explicit key set
 # --------------------------------------------------------------------------

@@ -232,3 +232,26 @@ def test_plan_counts_row_blocks(lib):
         pl = _lib.plan(9, heads, 1, n, n, 256)
         assert pl.grid >= blocks * pl.nsplit and pl.grid % 8 == 0
         assert blocks * pl.nsplit <= 256 or pl.chunk == 64
+
+
+def test_partials_plan_chunk_bounds(lib):
+    """A caller-made plan whose chunk exceeds MLAV_MAX_KV (the kernels take the
+    chunk as a 32-bit key count) is refused, whatever its split count."""
+    opt = _lib.options()
+    f = lib.mla_verify_partials
+
+    def c(nsplit, chunk, prefix=100):
+        plan = _lib.Plan(nsplit, 32, chunk, 0, 0)
+        return f(A, A, A, A, A, prefix, 0.07, A, A, 9, 64, ctypes.byref(plan), None, ctypes.byref(opt))
+
+    assert c(1, 1 << 40) == _lib.MLAV_ERR_ARG
+    assert c(1, 4000032) == _lib.MLAV_ERR_ARG
+    assert c(1, 48) == _lib.MLAV_ERR_ARG  # not a multiple of the tile
+    assert c(0, 64) == _lib.MLAV_ERR_ARG
+    assert c(3, 32, prefix=100) == _lib.MLAV_ERR_ARG  # 109 rows in chunks of 32 need 4 splits
+
+
+def test_combine_row_bound(lib):
+    f = lib.mla_verify_combine
+    assert f(A, A, 2, (1 << 24) + 64, A, A, None) == _lib.MLAV_ERR_SHAPE
+    assert f(A, A, 2, 1 << 34, A, A, None) == _lib.MLAV_ERR_SHAPE

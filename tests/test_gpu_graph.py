@@ -16,7 +16,7 @@ DEV = "cuda:0"
 
 @pytest.mark.parametrize("prefix,nsplit,merge", [(16384, 0, 0), (256, 0, 0), (150, 0, 1), (300, 1, 0)])
 def test_graph_replays_match_eager(prefix, nsplit, merge):
-    """merge = 1 at prefix 256: the split kernel merges its 3 splits (tickets
+    """merge = 1 at prefix 150: the split kernel merges its 3 splits (tickets
     in the workspace, reset by the last workgroup, same epoch on every replay)."""
     cases = [gen.make_case(9, prefix, tree="random", seed=500 + k) for k in range(3)]
     bufs = {k: getattr(cases[0], k).to(DEV) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}

@@ -91,13 +91,22 @@ def test_workloads_full_size(name):
 
 
 def test_chunk_boundaries():
+    """The benchmark workload's chunk (608 keys on 256 CUs) as an explicit plan, with the
+    sequence ending just before, at and just after one, two and three chunk
+    boundaries (mla_verify_partials splits exactly at multiples of the chunk;
+    the combine kernel merges)."""
     pl = api.device_plan(9, 1, 16393, 16393)
     c = int(pl.chunk)
-    for n in (c - 1, c, c + 1, 2 * c - 1, 2 * c + 1):
+    for n in (c - 1, c, c + 1, 2 * c - 1, 2 * c, 2 * c + 1, 3 * c):
         case = gen.make_case(9, n - 9, tree="random", seed=n)
-        out, lse = run(case)
+        d = dev_case(case)
+        plan = _lib.Plan(-(-n // c), 32, c, 0, 0)
+        po, pls = api.mla_verify_partials(d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"],
+                                          n - 9, case.scale, plan)
+        out, lse = api.combine(po, pls)
+        torch.cuda.synchronize()
         ro, rl = oracle(case)
-        assert_parity(out, lse, ro, rl, f"n={n} (chunk {c})")
+        assert_parity(out.cpu().view(9, 64, 512), lse.cpu().view(9, 64), ro, rl, f"n={n} (chunk {c})")
 
 
 # ---------------------------------------------------------------------------
@@ -208,6 +217,27 @@ def test_large_weights_without_restart():
     out, lse = run(case)
     ro, rl = oracle(case)
     assert_parity(out, lse, ro, rl, "weights near 2^100")
+
+
+@pytest.mark.parametrize("nsplit", [1, 0])
+def test_large_values_do_not_overflow_the_accumulators(nsplit):
+    """Values up to about 2^30 (inside the 2^31 precondition) under weights
+    near 2^95: the first tile's keys score 0, every later key scores 88 (about
+    127 in log2 units: below the score redo threshold), and all values are
+    positive, so a chunk's fp32 sums pass 2^128 unless the kernel redoes the
+    chunk with its own maximum as the reference. The exact result is the
+    mean of the later keys' values."""
+    case = gen.make_case(3, 2000, tree="chain", seed=33, num_heads=64)
+    case.q_nope.zero_()
+    case.q_rope.fill_(1.0)
+    case.scale = 1.0
+    case.k_rope[:32] = 0
+    case.k_rope[32:] = 1.375  # 64 x 1.375 = 88
+    case.kv_latent.copy_((case.kv_latent.float().abs() * 2.0 ** 28).to(torch.bfloat16))
+    assert case.kv_latent.float().abs().max().item() < 2.0 ** 31
+    ro, rl = oracle(case)
+    out, lse = run(case, nsplit=nsplit)
+    assert_parity(out, lse, ro, rl, f"values near 2^30, nsplit={nsplit}")
 
 
 def test_peaky_single_key_dominates():
