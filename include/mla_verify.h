@@ -71,6 +71,7 @@ extern "C" {
 #define MLAV_ERR_UNSUPPORTED 6 /* a valid but unimplemented configuration */
 #define MLAV_ERR_HIP 7         /* the HIP runtime reported an error */
 #define MLAV_ERR_ARG 8         /* a scalar or option value is invalid */
+#define MLAV_ERR_SCRATCH 9     /* mla_verify_noalloc: the call needs more than MLAV_SCRATCH_BYTES */
 
 #define MLAV_MAX_Q 64    /* q_len limit: one 64-bit ancestor mask per token */
 #define MLAV_ROWS 64     /* (token, head) rows per workgroup: one row block */
@@ -82,6 +83,7 @@ extern "C" {
 #define MLAV_MAX_POOL 4000000 /* rows of a paged KV pool (byte offsets into the pool's
                                  latent rows must stay below 2^32) */
 #define MLAV_MAX_COMBINE_ROWS (1 << 24) /* rows of one mla_verify_combine call */
+#define MLAV_SCRATCH_BYTES (24u << 20) /* static device scratch of mla_verify_noalloc (24 MiB) */
 
 /* Tuning knobs; a NULL options pointer means all zeros. */
 typedef struct mlav_options {
@@ -160,6 +162,29 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
                       float scale, float* out, float* lse, int32_t q_len, int32_t num_heads,
                       void* workspace, size_t workspace_bytes, void* stream,
                       const mlav_options* opt);
+
+/*
+ * mla_verify_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The split partials live in a static device array of MLAV_SCRATCH_BYTES
+ * that the library holds on each device it runs on until the process ends
+ * (its address is looked up once per device, on the first call there, with
+ * hipGetSymbolAddress). The call allocates nothing and calls no allocating
+ * routine; the caller still passes inputs and outputs. A call whose plan
+ * needs more partial storage than MLAV_SCRATCH_BYTES returns MLAV_ERR_SCRATCH
+ * and launches nothing: every plan the library makes by itself for one
+ * sequence with int16 partials fits (at most one workgroup per CU, 66 KB of
+ * partials each, about 17 MB on 256 CUs); forced large split counts or fp32
+ * partials may not. Every call on one device shares that device's array:
+ * calls that overlap on one device (two streams, two host threads) race and
+ * give undefined results; calls in stream order are safe (the array keeps
+ * the last call's contents, and nothing in it needs clearing). Arguments,
+ * options and errors otherwise as mla_verify_ex.
+ */
+int32_t mla_verify_noalloc(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                           const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
+                           float scale, float* out, float* lse, int32_t q_len, int32_t num_heads,
+                           void* stream, const mlav_options* opt);
 
 /*
  * Several sequences in one call: the pages' grid spans the batch as well as

@@ -21,11 +21,14 @@ MLAV_ERR_WORKSPACE = 5
 MLAV_ERR_UNSUPPORTED = 6
 MLAV_ERR_HIP = 7
 MLAV_ERR_ARG = 8
+MLAV_ERR_SCRATCH = 9
+MLAV_SCRATCH_BYTES = 24 << 20
 
 # the functions include/mla_verify.h declares
 EXPORTS = (
     "mla_verify",
     "mla_verify_ex",
+    "mla_verify_noalloc",
     "mla_verify_batched",
     "mla_verify_paged",
     "mla_verify_partials",
@@ -71,6 +74,9 @@ def load():
     lib.mla_verify.restype = c_int32
     lib.mla_verify_ex.argtypes = lib.mla_verify.argtypes + [POINTER(Options)]
     lib.mla_verify_ex.restype = c_int32
+    lib.mla_verify_noalloc.argtypes = tensors + [c_void_p, c_int64, c_float, c_void_p, c_void_p, c_int32,
+                                                 c_int32, c_void_p, POINTER(Options)]
+    lib.mla_verify_noalloc.restype = c_int32
     lib.mla_verify_batched.argtypes = tensors + [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_float,
                                                  c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
                                                  c_void_p, POINTER(Options)]

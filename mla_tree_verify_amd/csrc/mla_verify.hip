@@ -1558,6 +1558,29 @@ __global__ __launch_bounds__(kThreads) void combine_compact_wide_kernel(Args a, 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Static device scratch for callers that cannot allocate (mla_verify_noalloc):
+// the split partials of one call live here instead of in a caller workspace.
+// Each device holds its own copy for the life of the process. The array's
+// name is a host-side stand-in in host code; kernels get the device address
+// that hipGetSymbolAddress returns, looked up once per device.
+static __device__ __attribute__((aligned(256))) char scratch[MLAV_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device (looked up once per
+// device, with that device current), or nullptr on a HIP error.
+void* scratch_address() {
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  cache[dev].store(q, std::memory_order_release);
+  return q;
+}
+
 int device_cus(int32_t* out) {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -1789,11 +1812,13 @@ size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch
 
 namespace mlav {
 
-// One sequence: the body of mla_verify_ex.
+// One sequence: the body of mla_verify_ex and mla_verify_noalloc. With
+// `scratch_call`, the workspace is the static scratch and a plan that needs
+// more than it holds is refused with MLAV_ERR_SCRATCH.
 int verify_single(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
                   const void* k_rope, const int32_t* tree_parent, int64_t prefix_len, float scale,
                   float* out, float* lse, int32_t q_len, int32_t num_heads, void* workspace,
-                  size_t workspace_bytes, void* stream, const mlav_options* opt) {
+                  size_t workspace_bytes, void* stream, const mlav_options* opt, bool scratch_call) {
   int rc = common_checks(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, scale, out, lse,
                          q_len, num_heads, opt);
   if (rc != MLAV_OK) return rc;
@@ -1807,6 +1832,14 @@ int verify_single(const void* q_nope_absorbed, const void* q_rope, const void* k
   if (rc != MLAV_OK) return rc;
   const bool compact = compact_partials(opt);
   const size_t need = workspace_bytes_for(p, q_len, num_heads, 1, compact);
+  if (scratch_call) {
+    if (need > MLAV_SCRATCH_BYTES) return MLAV_ERR_SCRATCH;
+    if (need > 0) {
+      workspace = scratch_address();
+      if (!workspace) return MLAV_ERR_HIP;
+      workspace_bytes = MLAV_SCRATCH_BYTES;
+    }
+  }
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLAV_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return MLAV_ERR_ALIGN;
   Args a{};
@@ -1839,7 +1872,15 @@ int32_t mla_verify_ex(const void* q_nope_absorbed, const void* q_rope, const voi
                       void* workspace, size_t workspace_bytes, void* stream,
                       const mlav_options* opt) {
   return verify_single(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, prefix_len, scale, out,
-                       lse, q_len, num_heads, workspace, workspace_bytes, stream, opt);
+                       lse, q_len, num_heads, workspace, workspace_bytes, stream, opt, false);
+}
+
+int32_t mla_verify_noalloc(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
+                           const void* k_rope, const int32_t* tree_parent, int64_t prefix_len,
+                           float scale, float* out, float* lse, int32_t q_len, int32_t num_heads,
+                           void* stream, const mlav_options* opt) {
+  return verify_single(q_nope_absorbed, q_rope, kv_latent, k_rope, tree_parent, prefix_len, scale, out,
+                       lse, q_len, num_heads, nullptr, 0, stream, opt, true);
 }
 
 int32_t mla_verify(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
@@ -2031,6 +2072,7 @@ const char* mla_verify_strerror(int32_t status) {
     case MLAV_ERR_UNSUPPORTED: return "unsupported configuration";
     case MLAV_ERR_HIP: return "HIP runtime error";
     case MLAV_ERR_ARG: return "invalid scalar or option value";
+    case MLAV_ERR_SCRATCH: return "the call needs more than the static scratch (MLAV_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

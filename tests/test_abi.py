@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function(lib):
 
 def test_strerror(lib):
     assert _lib.strerror(0) == "ok"
-    for code in range(1, 9):
+    for code in range(1, 10):
         assert _lib.strerror(code) != "unknown status"
     assert _lib.strerror(99) == "unknown status"
 
