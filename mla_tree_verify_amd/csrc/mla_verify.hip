@@ -823,10 +823,34 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // score and the value phases the waves meet at a barrier, after which
     // each reads its partner's weights. kMasked selects the per-key
     // visibility test (and the first-visible-tile path).
-    auto step = [&](auto masked_tag, LDS_AS char* kbuf, LDS_AS char* vbuf, LDS_AS char* dma_buf, int i,
-                    uint32_t vis) {
+    // Tile i+1 landed (tile i+2 may still be in flight) and the partner
+    // scores of tile i are published once every wave passes the barrier;
+    // ring slot (i+3)%4 is free from then on.
+    auto advance = [&]() {
+      // only tile i+2's loads (and, paged, the page-table load before them) may be outstanding
+      if (kPaged)
+        __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+      lds_barrier();
+    };
+    // The first kAhead K-operand reads of the next step, issued before the
+    // last value MFMAs of the current one so that their LDS latency hides
+    // behind those MFMAs instead of stalling the next step's first score MFMA.
+    constexpr int kAhead = 8;
+    bf16x8_t kpre[kAhead];
+    auto prefetch_k = [&](LDS_AS char* nbuf) {
+#pragma unroll
+      for (int ks = 0; ks < kAhead; ++ks) {
+        kpre[ks] = lds_b128(nbuf + k_frag_off<kDh>(kb, ks));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // kbuf: tile i+1 (scores), vbuf: tile i (values), dma_buf: the slot that
+    // takes tile i+3, nbuf: tile i+2 (the next step's scores)
+    auto step = [&](auto masked_tag, LDS_AS char* kbuf, LDS_AS char* vbuf, LDS_AS char* dma_buf,
+                    LDS_AS char* nbuf, int i, uint32_t vis) {
       constexpr bool kMasked = decltype(masked_tag)::value;
-      constexpr int kAhead = 8;
       const int dma_rel = tile_rel(i + 3);
       auto kread = [&](int ks) {
         const int cc = 36 * kDh + 2 * ks;  // even chunk of the 576-d row
@@ -852,10 +876,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       __builtin_amdgcn_sched_barrier(0);
       bf16x8_t kf[18], vf[16];
 #pragma unroll
-      for (int ks = 0; ks < kAhead; ++ks) {
-        kf[ks] = kread(ks);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int ks = 0; ks < kAhead; ++ks) kf[ks] = kpre[ks];  // read during the previous step
 
       f32x16_t sc = {};
       float sv[8], pw[8];
@@ -948,9 +969,17 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
         __builtin_amdgcn_sched_barrier(0);
       }
       // values of tile i; tile loads in the first slots (each slot holds two
-      // MFMAs, so it has issue room to spare)
+      // MFMAs, so it has issue room to spare). Before the last kTail value
+      // slots the waves meet for the next step (tile i+2 landed, the partner
+      // scores of tile i+1 published) and the next step's first K operands
+      // are requested; those value MFMAs then cover the LDS latency.
+      constexpr int kTail = 2;
 #pragma unroll
       for (int nn = 0; nn < 16; ++nn) {
+        if (nn == 16 - kTail) {
+          advance();
+          prefetch_k(nbuf);
+        }
         const int j = frag(nn);
         acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], __builtin_bit_cast(bf16x8_t, ph[j >> 3]),
                                                              acc[j & 7], 0, 0, 0);
@@ -970,17 +999,6 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
       if constexpr (kPaged) idx_cur = idx_next;
     };
 
-    // Tile i+1 landed (tile i+2 may still be in flight) and the partner
-    // scores of tile i are published once every wave passes the barrier;
-    // ring slot (i+3)%4 is free from then on.
-    auto advance = [&](int) {
-      // only tile i+2's loads (and, paged, the page-table load before them) may be outstanding
-      if (kPaged)
-        __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
-      lds_barrier();
-    };
     // Tiles wholly inside the prefix and the chunk need no mask. Their loop
     // is unrolled by the ring period so that every step's slots are
     // compile-time objects; the remaining tiles take the masked step with the
@@ -989,38 +1007,34 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // loops keep a single register assignment per loop body.
     const int64_t full_end = prefix < c1 ? prefix : c1;
     const int n_full = full_end > c0 ? (int)((full_end - c0) / kTile) : 0;
+    // each step ends by meeting the other waves for the next one and reading
+    // its first K operands; the first step's are read here
+    advance();
+    prefetch_k(r1);
     int i = 0;
     for (; i + 4 <= n_full; i += 4) {
-      advance(i);
-      step(std::false_type{}, r1, r0, r3, i, 0u);
-      advance(i + 1);
-      step(std::false_type{}, r2, r1, r0, i + 1, 0u);
-      advance(i + 2);
-      step(std::false_type{}, r3, r2, r1, i + 2, 0u);
-      advance(i + 3);
-      step(std::false_type{}, r0, r3, r2, i + 3, 0u);
+      step(std::false_type{}, r1, r0, r3, r2, i, 0u);
+      step(std::false_type{}, r2, r1, r0, r3, i + 1, 0u);
+      step(std::false_type{}, r3, r2, r1, r0, i + 2, 0u);
+      step(std::false_type{}, r0, r3, r2, r1, i + 3, 0u);
     }
     // up to three more whole tiles: i is a multiple of 4 here, so their ring
     // slots are still compile-time objects
     if (i < n_full) {
-      advance(i);
-      step(std::false_type{}, r1, r0, r3, i, 0u);
+      step(std::false_type{}, r1, r0, r3, r2, i, 0u);
       ++i;
       if (i < n_full) {
-        advance(i);
-        step(std::false_type{}, r2, r1, r0, i, 0u);
+        step(std::false_type{}, r2, r1, r0, r3, i, 0u);
         ++i;
         if (i < n_full) {
-          advance(i);
-          step(std::false_type{}, r3, r2, r1, i, 0u);
+          step(std::false_type{}, r3, r2, r1, r0, i, 0u);
           ++i;
         }
       }
     }
     for (; i < ntiles; ++i) {
-      advance(i);
       const uint32_t vis = tile_visibility(c0 + (int64_t)i * kTile, c1, prefix, anc);
-      step(std::true_type{}, ring((i + 1) & 3), ring(i & 3), ring((i + 3) & 3), i, vis);
+      step(std::true_type{}, ring((i + 1) & 3), ring(i & 3), ring((i + 3) & 3), ring((i + 2) & 3), i, vis);
     }
     // Accumulator overflow: weights reach 2^96 before a redo, so values of
     // 2^32 / (keys in the chunk) and more can push a sum past fp32. The
