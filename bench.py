@@ -5,20 +5,24 @@
 
 One step = one full verify call (split-KV MFMA kernel + combine kernel) over one
 batch of synthetic bf16 inputs already resident in HBM. Prints one JSON line:
-value = algorithmic TFLOP/s of the whole call, measured on rotating input
-copies (more bytes than the 256 MB MALL, so every call reads its KV from HBM);
-the warm figure (same inputs every call) is reported beside it. `roofline`
-covers the split kernel, timed alone with HIP events on its stream;
-`cpu_baseline` times the fp64 oracle on the host cores.
+value = algorithmic TFLOP/s of the whole call on the headline workload,
+measured on rotating input copies (more bytes than the 256 MB MALL, so every
+call reads its KV from HBM); the warm figure (same inputs every call) is
+reported beside it. `roofline` covers the split kernel, timed alone with HIP
+events on its stream; `cpu_baseline` times the fp64 oracle on the host cores.
+`configs` times the other workloads (cold whole call, warm, split kernel
+alone) in the same run, and `measured_peaks` gives the bf16 MFMA throughput
+this GPU sustains under a pure MFMA load and a device-to-device copy rate.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
-import re
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -29,8 +33,11 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.
 PEAK_HBM_GBS = 8000.0
 SRC = os.path.join(ROOT, "mla_tree_verify_amd", "csrc", "mla_verify.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+PROBE_LIB = os.path.join(ROOT, "mla_tree_verify_amd", "libmla_verify_probe.so")
 # the pages' final sm_120 kernel at q_len 9, prefix 16384 (fp32, RTX PRO 6000): 4782.6 us
 PAGES_US_Q9_P16384 = 4782.6
+# the other workloads timed in the same run (the headline one is --workload)
+EXTRA_WORKLOADS = ("q9_p256", "q9_p4096", "q33_p16384_peaky", "q9_p65536_chain", "b8_ragged_q33")
 
 
 def parse():
@@ -45,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target host time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-extra-configs", action="store_true", help="time the headline workload only")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA and copy peak measurements")
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
                     help="after timing, run one device copy of this size (counter calibration)")
     ap.add_argument("--pv-mode", type=int, default=0)
@@ -111,6 +120,238 @@ def blas_threads() -> int:
     return os.cpu_count() or 1
 
 
+class Runner:
+    """One workload on the GPU: rotating input copies, prebuilt C-ABI
+    argument tuples for phase 0 (the whole call), 1 (split kernel alone) and
+    2 (combine kernel alone), and HIP-event timing on the library's stream.
+    Each timed call goes straight to the C ABI with prebuilt arguments, so that
+    host-side argument handling does not gap the back-to-back launches."""
+
+    def __init__(self, case, args, dev, heads, paged=False, pool_extra=0):
+        import torch
+
+        import oracle.mla_verify_oracle as orc
+        from mla_tree_verify_amd import _lib, api, gen
+
+        self.torch, self.case, self.args, self.dev = torch, case, args, dev
+        self.lib = _lib.load()
+        self._lib = _lib
+        q, H = case.q_len, heads
+        self.q, self.H = q, H
+        if case.batched:
+            offs = case.kv_offsets.tolist()
+            lens = [offs[b + 1] - offs[b] for b in range(len(offs) - 1)]
+            self.batch, self.total, self.max_kv = len(lens), offs[-1], max(lens)
+            parents = case.tree_parent.tolist()
+            self.flops = sum(orc.algorithmic_flops(parents[b], lens[b] - q, num_heads=H) for b in range(self.batch))
+            self.alg_bytes = sum(orc.algorithmic_bytes(q, lens[b], num_heads=H) for b in range(self.batch))
+        else:
+            n = case.prefix_len + q
+            self.batch, self.total, self.max_kv = 1, n, n
+            self.flops = orc.algorithmic_flops(case.tree_parent, case.prefix_len, num_heads=H)
+            self.alg_bytes = orc.algorithmic_bytes(q, n, num_heads=H)
+        self.plan = api.device_plan(q, self.batch, self.total, self.max_kv, nsplit=args.nsplit, pv_mode=args.pv_mode,
+                                    num_heads=H, partials=args.partials, merge=args.merge)
+        self.ws_bytes = _lib.workspace_size(q, H, self.batch, self.total, self.max_kv, nsplit=args.nsplit,
+                                            pv_mode=args.pv_mode, partials=args.partials, merge=args.merge)
+        host = {k: getattr(case, k) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
+        if case.batched:
+            host["kv_offsets"] = case.kv_offsets
+        self.paged = paged
+        if paged:
+            pg = gen.make_paged(case, seed=1234, extra_rows=pool_extra)
+            host["kv_latent"], host["k_rope"] = pg.pool_latent, pg.pool_rope
+            host["kv_index"] = pg.kv_index
+        out_shape = tuple(case.q_nope.shape[:-1]) + (512,)
+        lse_shape = tuple(case.q_nope.shape[:-1])
+        per_copy = (sum(t.numel() * t.element_size() for t in host.values()) + self.ws_bytes
+                    + self.batch * q * H * 513 * 4)
+        self.ncopy = max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))
+        self.copies = []
+        for _ in range(self.ncopy):
+            d = {k: v.to(dev) for k, v in host.items()}
+            d["out"] = torch.empty(out_shape, dtype=torch.float32, device=dev)
+            d["lse"] = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+            d["ws"] = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+            self.copies.append(d)
+        self.stream = torch.cuda.current_stream(dev)
+        opts = [_lib.options(args.nsplit, args.pv_mode, 0, args.partials, ph, args.merge) for ph in range(3)]
+        self.opts = opts  # the tuples below hold pointers into these
+        sc = ctypes.c_float(case.scale)
+        if paged:
+            self.entry = self.lib.mla_verify_paged
+        elif case.batched:
+            self.entry = self.lib.mla_verify_batched
+        else:
+            self.entry = self.lib.mla_verify_ex
+        for d in self.copies:
+            if paged:
+                offs_ptr = d["kv_offsets"].data_ptr() if case.batched else None
+                d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
+                              d["k_rope"].data_ptr(), d["kv_index"].data_ptr(), int(d["kv_latent"].shape[0]),
+                              d["tree_parent"].data_ptr(), offs_ptr, self.batch, self.total, self.max_kv, sc,
+                              d["out"].data_ptr(), d["lse"].data_ptr(), q, H, d["ws"].data_ptr(), self.ws_bytes,
+                              self.stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
+            elif case.batched:
+                d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
+                              d["k_rope"].data_ptr(), d["tree_parent"].data_ptr(), d["kv_offsets"].data_ptr(),
+                              self.batch, self.total, self.max_kv, sc, d["out"].data_ptr(), d["lse"].data_ptr(), q,
+                              H, d["ws"].data_ptr(), self.ws_bytes, self.stream.cuda_stream,
+                              ctypes.byref(opts[ph])) for ph in range(3)]
+            else:
+                d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
+                              d["k_rope"].data_ptr(), d["tree_parent"].data_ptr(), case.prefix_len, sc,
+                              d["out"].data_ptr(), d["lse"].data_ptr(), q, H, d["ws"].data_ptr(), self.ws_bytes,
+                              self.stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
+        for ph in range(3):
+            rc = self.entry(*self.copies[0]["args"][ph])
+            if rc != _lib.MLAV_OK:
+                raise _lib.MLAVError(rc, f"verify call (phase {ph})")
+
+    def call(self, d, phase=0):
+        self.entry(*d["args"][phase])
+
+    def warm(self, phase=0, rotate=True):
+        # W untimed steps, then more until warmup_ms of wall time has passed
+        t0 = time.perf_counter()
+        i = 0
+        while i < self.args.warmup or (time.perf_counter() - t0) * 1e3 < self.args.warmup_ms:
+            self.call(self.copies[i % self.ncopy] if rotate else self.copies[0], phase)
+            i += 1
+            if i % 50 == 0:
+                self.torch.cuda.synchronize()
+        self.torch.cuda.synchronize()
+
+    def timed(self, phase=0, rotate=True) -> float:
+        """us per call: K back-to-back launches between two events on the library's stream."""
+        torch = self.torch
+        self.warm(phase, rotate)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(self.args.steps):
+            self.call(self.copies[i % self.ncopy] if rotate else self.copies[0], phase)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / self.args.steps
+
+    def graph_us(self):
+        """The whole call replayed from a HIP graph (one graph makes the call on
+        every input copy in turn: cold, like the eager figure), and whether
+        the replayed output equals the eager one bit for bit."""
+        torch, _lib = self.torch, self._lib
+        d0 = self.copies[0]
+        self.call(d0)
+        torch.cuda.synchronize()
+        eager = (d0["out"].clone(), d0["lse"].clone())
+        d0["out"].zero_()
+        d0["lse"].zero_()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(self.dev)
+        with torch.cuda.graph(g, stream=cap):
+            for d in self.copies:
+                a = list(d["args"][0])
+                a[-2] = cap.cuda_stream  # inside the capture the launches go to the capture stream
+                rc = self.entry(*a)
+                if rc != _lib.MLAV_OK:
+                    raise _lib.MLAVError(rc, "verify call under graph capture")
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < 100.0:
+            g.replay()
+            torch.cuda.synchronize()
+        reps = max(1, self.args.steps // self.ncopy)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * self.ncopy)
+        equal = bool(torch.equal(d0["out"], eager[0]) and torch.equal(d0["lse"], eager[1]))
+        del g
+        return us, equal
+
+    def release(self):
+        self.copies = []
+        self.torch.cuda.empty_cache()
+
+
+def measured_peaks(torch, dev, num_cus: int) -> dict:
+    """bf16 MFMA throughput under a pure MFMA load (the probe library: one
+    wave per SIMD on every CU issuing independent 32x32x16 MFMAs) and the
+    rate of a 1 GiB device-to-device copy (bytes read + written)."""
+    res = {}
+    if os.path.exists(PROBE_LIB):
+        probe = ctypes.CDLL(PROBE_LIB)
+        probe.mlav_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        probe.mlav_probe_mfma.restype = ctypes.c_int32
+        probe.mlav_probe_mfma_per_wave.restype = ctypes.c_int32
+        grid, iters = num_cus, 4000
+        out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+        cyc = torch.empty(grid * 4, dtype=torch.int64, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        for _ in range(3):
+            if probe.mlav_probe_mfma(grid, iters, out.data_ptr(), cyc.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("MFMA probe launch failed")
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        probe.mlav_probe_mfma(grid, iters, out.data_ptr(), cyc.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        per_wave = probe.mlav_probe_mfma_per_wave()
+        mfmas = grid * 4 * iters * per_wave
+        cycles = float(cyc.double().mean().item())
+        res["mfma_bf16_tflops"] = round(mfmas * 32768 / (ms * 1e-3) / 1e12, 1)
+        res["mfma_clock_ghz"] = round(cycles / (ms * 1e-3) / 1e9, 3)  # shader clock under the MFMA load
+        res["mfma_cycles_per_instruction"] = round(cycles / (iters * per_wave), 2)
+        res["mfma_probe"] = (f"{grid} workgroups x 4 waves (one per SIMD), {iters * per_wave} independent "
+                             "v_mfma_f32_32x32x16_bf16 per wave over 8 accumulators")
+    nb = 1 << 30
+    src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    res["hbm_copy_gbs"] = round(2 * nb / (ms * 1e-3) / 1e9, 1)
+    res["hbm_copy"] = "1 GiB fp32 device-to-device copy (torch copy_), read + written bytes"
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
+def config_summary(r: Runner, us: float, us_warm: float, split_us: float, peaks: dict) -> dict:
+    tf = r.flops / (us * 1e-6) / 1e12
+    d = {"us_per_call": round(us, 2), "us_per_call_warm": round(us_warm, 2), "split_kernel_us": round(split_us, 2),
+         "tflops": round(tf, 2), "pct_mfma_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+         "split_kernel_tflops": round(r.flops / (split_us * 1e-6) / 1e12, 2),
+         "split_kernel_frac": round(r.flops / (split_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+         "hbm_gbs_algorithmic": round(r.alg_bytes / (us * 1e-6) / 1e9, 1),
+         "pct_hbm_peak": round(100 * r.alg_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+         "algorithmic_gflop": round(r.flops / 1e9, 3), "algorithmic_mb": round(r.alg_bytes / 1e6, 3),
+         "nsplit": int(r.plan.nsplit), "chunk": int(r.plan.chunk), "batch": r.batch, "q_len": r.q,
+         "kv_rows": r.total}
+    if peaks.get("mfma_bf16_tflops"):
+        d["pct_measured_mfma_peak"] = round(100 * tf / peaks["mfma_bf16_tflops"], 2)
+    if r.case.batched:
+        d["prefixes"] = list(r.case.prefix_lens)
+    return d
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -121,169 +362,45 @@ def main() -> int:
                           "n_gpus": args.gpus}))
         return 2
 
-    import ctypes
-
     import numpy as np
     import torch
 
     import oracle.mla_verify_oracle as orc
-    from mla_tree_verify_amd import _lib, api, gen
+    from mla_tree_verify_amd import _lib, gen
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    _lib.load()
+    peaks = {} if args.no_peaks else measured_peaks(torch, dev, num_cus)
+
     spec = gen.WORKLOADS[args.workload]
-    if spec["kind"] != "single":
-        print(json.dumps({"error": "bench.py times single-sequence workloads"}))
+    H = args.heads
+    if spec["kind"] != "single" and (args.heads != 64 or args.prefix >= 0):
+        print(json.dumps({"error": "--heads and --prefix apply to single-sequence workloads"}))
         return 2
     if args.heads == 64 and args.prefix < 0:
         case = gen.make_workload(args.workload)
     else:
-        kw = dict(gen.WORKLOADS[args.workload])
+        kw = dict(spec)
         kw.pop("kind")
         if args.prefix >= 0:
             kw["prefix_len"] = args.prefix
         case = gen.make_case(num_heads=args.heads, **kw)
+    run = Runner(case, args, dev, H, paged=args.paged, pool_extra=args.pool_extra)
     q, p = case.q_len, case.prefix_len
-    n = p + q
-    H = args.heads
-    flops = orc.algorithmic_flops(case.tree_parent, p, num_heads=H)
-    alg_bytes = orc.algorithmic_bytes(q, n, num_heads=H)
-    plan = api.device_plan(q, 1, n, n, nsplit=args.nsplit, pv_mode=args.pv_mode, num_heads=H,
-                           partials=args.partials, merge=args.merge)
-    lib = _lib.load()
-    ws_bytes = _lib.workspace_size(q, H, 1, n, n, nsplit=args.nsplit, pv_mode=args.pv_mode, partials=args.partials,
-                                   merge=args.merge)
+    plan = run.plan
 
-    host = {k: getattr(case, k) for k in ("q_nope", "q_rope", "kv_latent", "k_rope", "tree_parent")}
-    if args.paged:
-        pg = gen.make_paged(case, seed=1234, extra_rows=args.pool_extra)
-        host["kv_latent"], host["k_rope"] = pg.pool_latent, pg.pool_rope
-        host["kv_index"] = pg.kv_index
-    per_copy = sum(t.numel() * t.element_size() for t in host.values()) + ws_bytes + q * H * 513 * 4
-    ncopy = max(2, math.ceil(args.rotate_mb * 2**20 / per_copy))
-    copies = []
-    for _ in range(ncopy):
-        d = {k: v.to(dev) for k, v in host.items()}
-        d["out"] = torch.empty(q, H, 512, dtype=torch.float32, device=dev)
-        d["lse"] = torch.empty(q, H, dtype=torch.float32, device=dev)
-        d["ws"] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-        copies.append(d)
-    stream = torch.cuda.current_stream(dev)
-    # Each timed call goes straight to the C ABI with prebuilt arguments, so
-    # that host-side argument handling does not gap the back-to-back launches.
-    # phase 0 = the whole call, 1 = the split kernel alone, 2 = the combine
-    # kernel alone (on the workspace phase 1 filled; nothing when the split
-    # kernel merges the splits itself).
-    opts = [_lib.options(args.nsplit, args.pv_mode, 0, args.partials, ph, args.merge) for ph in range(3)]
-    entry = lib.mla_verify_paged if args.paged else lib.mla_verify_ex
-    for d in copies:
-        if args.paged:
-            d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
-                          d["k_rope"].data_ptr(), d["kv_index"].data_ptr(), int(d["kv_latent"].shape[0]),
-                          d["tree_parent"].data_ptr(), None, 1, n, n, ctypes.c_float(case.scale),
-                          d["out"].data_ptr(), d["lse"].data_ptr(), q, H, d["ws"].data_ptr(), ws_bytes,
-                          stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
-        else:
-            d["args"] = [(d["q_nope"].data_ptr(), d["q_rope"].data_ptr(), d["kv_latent"].data_ptr(),
-                          d["k_rope"].data_ptr(), d["tree_parent"].data_ptr(), p, ctypes.c_float(case.scale),
-                          d["out"].data_ptr(), d["lse"].data_ptr(), q, H, d["ws"].data_ptr(), ws_bytes,
-                          stream.cuda_stream, ctypes.byref(opts[ph])) for ph in range(3)]
-    for ph in range(3):
-        rc = entry(*copies[0]["args"][ph])
-        if rc != _lib.MLAV_OK:
-            raise _lib.MLAVError(rc, f"verify call (phase {ph})")
-
-    def call(d):
-        entry(*d["args"][0])
-
-    def warm(fn, rotate: bool = True) -> None:
-        # W untimed steps, then more until warmup_ms of wall time has passed
-        t0 = time.perf_counter()
-        i = 0
-        while i < args.warmup or (time.perf_counter() - t0) * 1e3 < args.warmup_ms:
-            fn(copies[i % ncopy] if rotate else copies[0])
-            i += 1
-            if i % 50 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-
-    def timed(rotate: bool) -> float:
-        warm(call, rotate)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(args.steps):
-            call(copies[i % ncopy] if rotate else copies[0])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / args.steps  # us per call
-
-    us_warm = timed(rotate=False)
-    us_cold = timed(rotate=True)
-
-    # each kernel alone: K back-to-back launches (rotating inputs) between two
-    # events recorded on the stream the library launches on
-    def split(d):
-        entry(*d["args"][1])
-
-    def merge(d):
-        entry(*d["args"][2])
-
-    def batch_us(fn) -> float:
-        warm(fn)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(args.steps):
-            fn(copies[i % ncopy])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / args.steps
-
-    split_us = batch_us(split)
-    combine_us = batch_us(merge) if plan.combine == 1 else 0.0
-
-    # The whole call replayed from a HIP graph, as a serving loop would issue
-    # it: one graph makes the call on every input copy in turn (cold, like
-    # us_cold). Inside the capture the launches go to the capture stream, so
-    # the arguments carry that stream. The replayed output must equal the
-    # eager output bit for bit (the kernels are deterministic).
+    us_warm = run.timed(0, rotate=False)
+    us_cold = run.timed(0, rotate=True)
+    split_us = run.timed(1)
+    combine_us = run.timed(2) if plan.combine == 1 else 0.0
     graph_us = graph_equal = None
     if not args.no_graph:
-        d0 = copies[0]
-        call(d0)
-        torch.cuda.synchronize()
-        eager = (d0["out"].clone(), d0["lse"].clone())
-        d0["out"].zero_()
-        d0["lse"].zero_()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream(dev)
-        with torch.cuda.graph(g, stream=cap):
-            for d in copies:
-                a = list(d["args"][0])
-                a[-2] = cap.cuda_stream
-                rc = entry(*a)
-                if rc != _lib.MLAV_OK:
-                    raise _lib.MLAVError(rc, "verify call under graph capture")
-        t0 = time.perf_counter()
-        while (time.perf_counter() - t0) * 1e3 < 100.0:
-            g.replay()
-            torch.cuda.synchronize()
-        reps = max(1, args.steps // ncopy)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        graph_us = e0.elapsed_time(e1) * 1e3 / (reps * ncopy)
-        graph_equal = bool(torch.equal(d0["out"], eager[0]) and torch.equal(d0["lse"], eager[1]))
-        del g
+        graph_us, graph_equal = run.graph_us()
 
     if args.copy_calib_mb > 0:
         nb = int(args.copy_calib_mb * 2**20) // 4 * 4
@@ -294,8 +411,8 @@ def main() -> int:
         torch.cuda.synchronize()
 
     # parity of the benchmarked output against the oracle (also the CPU baseline)
-    d0 = copies[0]
-    call(d0)
+    d0 = run.copies[0]
+    run.call(d0)
     torch.cuda.synchronize()
     out = d0["out"].cpu().double().numpy()
     lse = d0["lse"].cpu().double().numpy()
@@ -307,24 +424,55 @@ def main() -> int:
         t_start = time.perf_counter()
         while True:
             t0 = time.perf_counter()
-            ro, rl = orc.mla_verify(case.q_nope, case.q_rope, case.kv_latent, case.k_rope, case.tree_parent, p,
-                                    case.scale)
+            if case.batched:
+                ro, rl = orc.mla_verify_batched(case.q_nope, case.q_rope, case.kv_latent, case.k_rope,
+                                                case.tree_parent, case.kv_offsets, case.scale)
+            else:
+                ro, rl = orc.mla_verify(case.q_nope, case.q_rope, case.kv_latent, case.k_rope, case.tree_parent,
+                                        p, case.scale)
             t_cpu += time.perf_counter() - t0
             reps += 1
             if t_cpu >= args.cpu_seconds or time.perf_counter() - t_start > 30.0:
                 break
-        cpu = {"value": flops * reps / t_cpu / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+        try:
+            affinity = len(os.sched_getaffinity(0))
+        except AttributeError:
+            affinity = None
+        cpu = {"value": run.flops * reps / t_cpu / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
                "sample": f"the full {args.workload} workload, {reps} oracle call(s), fp64 numpy, "
-                         f"{t_cpu:.1f} s; us/call {t_cpu / reps * 1e6:.0f}"}
+                         f"{t_cpu:.1f} s; us/call {t_cpu / reps * 1e6:.0f}",
+               "blas_threads": blas_threads(), "os_cpu_count": os.cpu_count(), "sched_affinity_cores": affinity}
         err = np.abs(out - ro)
         parity = {"max_abs_err": float(err.max()),
                   "worst_err_over_tol": float((err / (2e-3 + 1e-2 * np.abs(ro))).max()),
                   "lse_max_abs_err": float(np.abs(lse - rl).max())}
 
+    flops, alg_bytes = run.flops, run.alg_bytes
     tflops = flops / (us_cold * 1e-6) / 1e12
     tflops_warm = flops / (us_warm * 1e-6) / 1e12
     achieved = flops / (split_us * 1e-6) / 1e12
     traffic, mfma_busy = read_counters(args.workload, args.paged) if H == 64 else (None, None)
+    headline_plain = (args.workload == "q9_p16384" and H == 64 and not args.paged and args.prefix < 0)
+    run.release()
+
+    # the other workloads, same run: cold whole call, warm, split kernel alone
+    configs = {}
+    if not args.no_extra_configs:
+        for name in EXTRA_WORKLOADS:
+            if name == args.workload:
+                continue
+            r = Runner(gen.make_workload(name), args, dev, 64)
+            u_cold = r.timed(0, rotate=True)
+            u_warm = r.timed(0, rotate=False)
+            u_split = r.timed(1)
+            configs[name] = config_summary(r, u_cold, u_warm, u_split, peaks)
+            c_traffic, c_busy = read_counters(name)
+            if c_traffic is not None:
+                configs[name]["split_kernel_hbm_bytes"] = c_traffic
+            if c_busy is not None:
+                configs[name]["split_kernel_mfma_busy"] = c_busy
+            r.release()
+
     res = {
         "metric": "MLA verify attention us/call + TFLOP/s (% MFMA peak), H=64 q_len=9, prefix 16k",
         "value": round(tflops, 2),
@@ -335,15 +483,14 @@ def main() -> int:
         "ms_per_step": round(us_cold / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(tflops / (flops / (PAGES_US_Q9_P16384 * 1e-6) / 1e12), 2)
-        if args.workload == "q9_p16384" and H == 64 and not args.paged and args.prefix < 0 else None,
+        "vs_baseline": round(tflops / (flops / (PAGES_US_Q9_P16384 * 1e-6) / 1e12), 2) if headline_plain else None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": n, "heads": H, "dl": 512,
+        "config": {"workload": args.workload, "q_len": q, "prefix": p, "kv_len": run.total, "heads": H, "dl": 512,
                    "dr": 64, "tree": case.meta["tree"], "scale": case.scale, "nsplit": plan.nsplit,
                    "chunk": plan.chunk, "pv_mode": args.pv_mode, "partials": "int16" if args.partials == 0 else "fp32",
                    "merge": ["none (one split)", "combine kernel", "in the split kernel"][plan.combine],
-                   "kv_layout": (f"paged, one token per page, pool {n + args.pool_extra} rows" if args.paged
+                   "kv_layout": (f"paged, one token per page, pool {run.total + args.pool_extra} rows" if args.paged
                                  else "contiguous"),
                    "parallelism": "single GPU"},
         "us_per_call": round(us_cold, 2),
@@ -352,6 +499,8 @@ def main() -> int:
         "graph_replay_equals_eager": graph_equal,
         "tflops_warm": round(tflops_warm, 2),
         "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "pct_measured_mfma_peak": (round(100 * tflops / peaks["mfma_bf16_tflops"], 2)
+                                   if peaks.get("mfma_bf16_tflops") else None),
         "hbm_gbs_algorithmic": round(alg_bytes / (us_cold * 1e-6) / 1e9, 1),
         "pct_hbm_peak": round(100 * alg_bytes / (us_cold * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "split_kernel_us": round(split_us, 2),
@@ -364,6 +513,8 @@ def main() -> int:
                      "mfma_busy_counter": mfma_busy},
         "cpu_baseline": cpu,
         "parity": parity,
+        "measured_peaks": peaks or None,
+        "configs": configs or None,
         "baseline_note": "vs_baseline divides by the pages' final sm_120 kernel at q9/16k (4782.6 us, fp32, RTX PRO "
                          "6000): context from other hardware, not a target",
     }

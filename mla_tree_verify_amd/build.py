@@ -18,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "mla_verify.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_verify.so")
+# the benchmark's MFMA peak probe (not part of the verify path)
+PROBE_SRC = os.path.join(PKG, "csrc", "peak_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libmla_verify_probe.so")
 
 
 def hipcc() -> str:
@@ -45,9 +48,9 @@ def compile_flags(resource_usage: bool = False):
     return flags
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + compile_flags(resource_usage) + [SRC, "-o", tmp]
+def _compile(src: str, lib: str, verbose: bool, resource_usage: bool) -> str:
+    tmp = lib + ".tmp"
+    cmd = [hipcc()] + compile_flags(resource_usage) + [src, "-o", tmp]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the gfx feature name; that warning is harmless
     noise = "not a recognized feature for this target"
@@ -56,8 +59,14 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> str:
+    """Builds libmla_verify.so and the benchmark's probe library; returns the former's path."""
+    _compile(PROBE_SRC, PROBE_LIB, verbose, False)
+    return _compile(SRC, LIB, verbose, resource_usage)
 
 
 if __name__ == "__main__":

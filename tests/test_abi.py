@@ -255,3 +255,27 @@ def test_combine_row_bound(lib):
     f = lib.mla_verify_combine
     assert f(A, A, 2, (1 << 24) + 64, A, A, None) == _lib.MLAV_ERR_SHAPE
     assert f(A, A, 2, 1 << 34, A, A, None) == _lib.MLAV_ERR_SHAPE
+
+
+def test_probe_library_exports_its_header():
+    """The benchmark's MFMA peak probe: a separate library with its own header."""
+    path = os.path.join(ROOT, "mla_tree_verify_amd", "libmla_verify_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    text = open(os.path.join(ROOT, "include", "mla_verify_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(mlav_probe\w*)\s*\(", text)))
+    assert declared == ["mlav_probe_mfma", "mlav_probe_mfma_per_wave"]
+    probe = ctypes.CDLL(path)
+    for name in declared:
+        assert hasattr(probe, name)
+    probe.mlav_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    probe.mlav_probe_mfma.restype = ctypes.c_int32
+    buf = ctypes.create_string_buffer(64)
+    # argument errors are caught on the host, before any launch
+    assert probe.mlav_probe_mfma(0, 10, buf, buf, None) == 2
+    assert probe.mlav_probe_mfma(1, 0, buf, buf, None) == 2
+    assert probe.mlav_probe_mfma(1, 10, None, buf, None) == 2
+    assert probe.mlav_probe_mfma(1, 10, buf, None, None) == 2
+    assert probe.mlav_probe_mfma_per_wave() == 16
