@@ -127,6 +127,7 @@ struct Args {
   int32_t nwork;
   int32_t per_xcd;
   int32_t fixed_ns;      // combine only: >0 forces every row's split count
+  int32_t list_run;      // >0: batched chunk list dealt to the XCDs in runs of this many items
 };
 
 // ---------------------------------------------------------------------------
@@ -307,6 +308,157 @@ __device__ inline bool decode_work(const Args& a, int& b, int& s, int& t) {
   s = uniform(bs % a.nsplit);
   b = uniform(bs / a.nsplit);
   return true;
+}
+
+// Batched calls: the chunks of every sequence form one list, in this order:
+//   1. one entry per sequence whose offsets are inconsistent (its NaN rows),
+//   2. every full chunk (`chunk` keys), by sequence, then split,
+//   3. each sequence's last, shorter chunk; up to 64 sequences longest first
+//      (16 length classes of chunk / 16 keys, each class in sequence order),
+//      beyond that in sequence order,
+// so that the long work starts first and the short tail chunks fill the CUs
+// at the end (an XCD hands its workgroups to its CUs in id order). Item i of
+// the list is row block i % nrb of chunk i / nrb. The dispatcher sends
+// workgroup id w to XCD w % 8; ids map to items so that each XCD takes runs
+// of list_run consecutive items (row blocks of one chunk, sharing its KV in
+// that XCD's L2), the runs dealt over the XCDs in rounds of 8, every other
+// round in reverse order (the longest runs do not all land on the same XCDs).
+// Every wave computes the same (uniform) result from the offsets, one
+// sequence per lane.
+
+// One sequence per lane: bounds check, full chunks and the length class of
+// the last, shorter chunk (-1: none).
+__device__ inline void list_lane(const Args& a, int sb, bool& ok, int64_t& r0, int& len, int& f, int& cls) {
+  ok = false;
+  r0 = 0;
+  len = 0;
+  f = 0;
+  cls = -1;
+  if (sb < a.batch) {
+    r0 = a.offs[sb];
+    const int64_t r1 = a.offs[sb + 1];
+    const int64_t n = r1 - r0;
+    ok = r0 >= 0 && r1 <= a.total_kv && n >= a.q && n <= a.max_kv;
+    if (ok) {
+      const uint32_t c = (uint32_t)a.chunk;  // chunk and n are at most MLAV_MAX_KV
+      len = (int)n;
+      f = (int)((uint32_t)len / c);
+      const uint32_t rem = (uint32_t)len - (uint32_t)f * c;
+      cls = rem > 0 ? (int)(rem * 16u / c) : -1;
+    }
+  }
+}
+
+__device__ inline int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Lanes of m below this lane.
+__device__ inline int mask_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ inline int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ inline int64_t readlane_i64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Work id -> (sequence, split, row block) through the chunk list, with the
+// sequence's first row and length; ok = false for an inconsistent sequence
+// (split 0: write its NaN rows). False past the list's end.
+__device__ inline bool decode_list(const Args& a, int& b, int& s, int& t, int64_t& row0, int64_t& n, bool& ok) {
+  const int bid = blockIdx.x;
+  const int g = a.list_run;
+  const int j = bid / kXcds;  // the j-th workgroup dispatched on XCD bid % 8
+  const int rnd = j / g;      // round of runs: run rnd * 8 + x goes to XCD x, reversed every other round
+  const int x = (rnd & 1) ? kXcds - 1 - bid % kXcds : bid % kXcds;
+  const int item = uniform((rnd * kXcds + x) * g + j % g);
+  int k = uniform(item / a.nrb);  // list entry
+  t = uniform(item % a.nrb);
+  const int lane = threadIdx.x & 63;
+  const int B = a.batch;
+  bool lok;
+  int64_t lr0;
+  int llen, lf, lcls;
+  // sets the outputs from lane L of the current group
+  auto take = [&](int g0, int L, int split, bool valid) {
+    b = g0 + L;
+    s = split;
+    ok = valid;
+    row0 = valid ? readlane_i64(lr0, L) : 0;
+    n = valid ? readlane_i(llen, L) : 0;
+  };
+  if (B <= 64) {
+    list_lane(a, lane, lok, lr0, llen, lf, lcls);
+    const uint64_t inv = __ballot(lane < B && !lok);
+    const int ninv = __popcll(inv);
+    if (k < ninv) {
+      take(0, __builtin_ctzll(__ballot(lane < B && !lok && mask_rank(inv) == k)), 0, false);
+      return true;
+    }
+    k -= ninv;
+    const int incl = wave_incl_scan(lf, lane);
+    const int nfull = readlane_i(incl, 63);
+    if (k < nfull) {
+      const int L = __builtin_ctzll(__ballot(incl > k));
+      take(0, L, k - (readlane_i(incl, L) - readlane_i(lf, L)), true);
+      return true;
+    }
+    k -= nfull;
+    // rank of each lane's last chunk: longer classes first, then sequence order
+    int pos = -1, base = 0;
+#pragma unroll
+    for (int c = 15; c >= 0; --c) {
+      const uint64_t m = __ballot(lcls == c);
+      if (lcls == c) pos = base + mask_rank(m);
+      base += __popcll(m);
+    }
+    if (k >= base) return false;
+    const int L = __builtin_ctzll(__ballot(pos == k));
+    take(0, L, readlane_i(lf, L), true);
+    return true;
+  }
+  // more than 64 sequences: section sizes first, then the search
+  int ninv = 0, nfull = 0, npart = 0;
+  for (int g0 = 0; g0 < B; g0 += 64) {
+    list_lane(a, g0 + lane, lok, lr0, llen, lf, lcls);
+    ninv += __popcll(__ballot(g0 + lane < B && !lok));
+    nfull += readlane_i(wave_incl_scan(lf, lane), 63);
+    npart += __popcll(__ballot(lcls >= 0));
+  }
+  const int sec = k < ninv ? 0 : k < ninv + nfull ? 1 : k < ninv + nfull + npart ? 2 : -1;
+  if (sec < 0) return false;
+  int rank = sec == 0 ? k : sec == 1 ? k - ninv : k - ninv - nfull;
+  for (int g0 = 0; g0 < B; g0 += 64) {
+    list_lane(a, g0 + lane, lok, lr0, llen, lf, lcls);
+    if (sec == 1) {
+      const int incl = wave_incl_scan(lf, lane);
+      const int tot = readlane_i(incl, 63);
+      if (rank < tot) {
+        const int L = __builtin_ctzll(__ballot(incl > rank));
+        take(g0, L, rank - (readlane_i(incl, L) - readlane_i(lf, L)), true);
+        return true;
+      }
+      rank -= tot;
+    } else {
+      const bool mine = sec == 0 ? (g0 + lane < B && !lok) : (lcls >= 0);
+      const uint64_t m = __ballot(mine);
+      if (rank < __popcll(m)) {
+        const int L = __builtin_ctzll(__ballot(mine && mask_rank(m) == rank));
+        take(g0, L, sec == 0 ? 0 : readlane_i(lf, L), sec != 0);
+        return true;
+      }
+      rank -= __popcll(m);
+    }
+  }
+  return false;
 }
 
 // NaN into the output rows of row block rbk of sequence b (inconsistent offsets).
@@ -1216,14 +1368,21 @@ void split_mfma_kernel(Args a) {
   // loads (fetched lazily, each group would wait on its own round trip).
   asm volatile("" ::"s"(a.qn), "s"(a.qr), "s"(a.lat), "s"(a.rope), "s"(a.parent), "s"(a.offs),
                "s"(a.single_n), "s"(a.total_kv), "s"(a.max_kv), "s"(a.chunk), "s"(a.scale_log2), "s"(a.q),
-               "s"(a.heads), "s"(a.nrb), "s"(a.nsplit), "s"(a.nwork), "s"(a.per_xcd));
+               "s"(a.heads), "s"(a.nrb), "s"(a.nsplit), "s"(a.nwork), "s"(a.per_xcd), "s"(a.batch),
+               "s"(a.list_run));
   int b, s, t;  // t: the row block
-  if (!decode_work(a, b, s, t)) return;
+  int64_t row0, n;
+  bool ok;
+  if (a.list_run > 0) {
+    if (!decode_list(a, b, s, t, row0, n, ok)) return;
+  } else {
+    if (!decode_work(a, b, s, t)) return;
+    ok = seq_bounds(a, b, row0, n);
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  int64_t row0, n;
-  if (!seq_bounds(a, b, row0, n)) {
+  if (!ok) {
     if (s == 0) write_nan_rows(a, b, t, tid, kThreads);
     return;
   }
@@ -1631,6 +1790,90 @@ bool compact_partials(const mlav_options* opt) {
 // Row blocks of one sequence: its q * heads (token, head) rows in blocks of 64.
 int32_t row_blocks(int32_t q, int32_t heads) { return (q * heads + kRows - 1) / kRows; }
 
+int64_t round_chunk(int64_t c) {
+  c = (c + kChunkGran - 1) / kChunkGran * kChunkGran;
+  return c < kMinChunk ? kMinChunk : c;
+}
+
+// A workgroup's fixed cost (start-up loads, partial writes, its share of
+// the combine) in tile steps, for the planner's estimates.
+constexpr int64_t kFixedTiles = 12;
+
+// Items of the batched chunk list dealt to one XCD in a row (one is a row
+// block): runs of up to 8 row blocks of one chunk share its KV in an L2.
+constexpr int32_t kListRun = 8;
+int32_t list_run(int32_t nrb) { return nrb < kListRun ? nrb : kListRun; }
+
+// Chunk length of a batched call, from the host copies of its total and
+// longest lengths (the per-sequence lengths stay on the device).
+//  - Unequal lengths: about two workgroups per CU over the whole batch (the
+//    chunk list, long chunks first, evens out the different lengths; fewer,
+//    longer chunks leave the last round unbalanced, more, shorter ones pay
+//    the fixed cost more often). Below kSmallChunk keys per chunk the fixed
+//    cost dominates, and the estimate below decides, up to kSmallChunk.
+//  - Equal lengths (total = batch x max): every chunk is alike; of the
+//    candidates (the longest sequence cut into 1, 2, 3, ... chunks), the one
+//    whose workgroups fill the CUs in the fewest tile steps, each workgroup
+//    paying its fixed cost.
+// Estimate for unequal lengths, in tile steps of one CU: the total work
+// spread over the CUs, with every workgroup's fixed cost (the chunks number
+// about total / chunk + batch / 2), plus half a workgroup of tail; at least
+// one whole workgroup.
+constexpr int64_t kSmallChunk = 256;
+int64_t batched_chunk(int64_t nrb, int32_t batch, int64_t total_kv, int64_t max_kv, int32_t num_cus) {
+  const bool equal = total_kv == (int64_t)batch * max_kv;
+  const int64_t cmax = round_chunk(max_kv);
+  if (!equal) {
+    const int64_t c = round_chunk((nrb * total_kv + 2 * (int64_t)num_cus - 1) / (2 * (int64_t)num_cus));
+    if (c >= kSmallChunk) return c < cmax ? c : cmax;
+  }
+  const int64_t cus_per_xcd = num_cus >= kXcds ? num_cus / kXcds : 1;
+  const double work = (double)nrb * ((double)total_kv / kTile);  // tile steps of the whole batch
+  int64_t best = cmax, prev = -1;
+  double best_cost = -1.0;
+  for (int64_t ns = 1; ns <= 4096; ++ns) {
+    const int64_t c = round_chunk((max_kv + ns - 1) / ns);
+    if (c == prev) continue;
+    prev = c;
+    const double item = (double)((c + kTile - 1) / kTile + kFixedTiles);
+    double cost;
+    if (equal) {
+      const int64_t items = nrb * batch * ((max_kv + c - 1) / c);
+      const int64_t rounds = ((items + kXcds - 1) / kXcds + cus_per_xcd - 1) / cus_per_xcd;
+      cost = (double)rounds * item;
+    } else {
+      const double chunks = (double)total_kv / (double)c + 0.5 * batch;
+      cost = (work + (double)nrb * chunks * kFixedTiles) / num_cus + 0.5 * item;
+      if (cost < item) cost = item;
+    }
+    if (best_cost < 0.0 || cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+    if (c <= kMinChunk) break;
+  }
+  if (!equal && best > kSmallChunk) best = kSmallChunk < cmax ? kSmallChunk : cmax;
+  return best;
+}
+
+// Batched calls with unequal lengths run through the chunk list; equal
+// lengths keep the (sequence, split, row block) order in one range per XCD,
+// which has no empty items then.
+bool chunk_list(int32_t batch, int64_t total_kv, int64_t max_kv) {
+  return batch > 1 && total_kv != (int64_t)batch * max_kv;
+}
+
+// Grid of a batched call: covers the chunk list of any offsets that meet the
+// contract (non-decreasing from 0 to total_kv, so that the chunks number at
+// most ceil(total_kv / chunk) + batch - 1), dealt in runs of list_run(nrb).
+int64_t list_grid(int64_t nrb, int32_t batch, int64_t total_kv, int64_t chunk, int64_t ns) {
+  int64_t mcap = (total_kv + chunk - 1) / chunk + batch - 1;
+  if (mcap > (int64_t)batch * ns) mcap = (int64_t)batch * ns;
+  const int64_t run = list_run((int32_t)nrb);
+  const int64_t runs = (mcap * nrb + run - 1) / run;
+  return (runs + kXcds - 1) / kXcds * kXcds * run;
+}
+
 int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t max_kv,
               int32_t num_cus, const mlav_options* opt, mlav_plan* p) {
   if (q < 1 || q > MLAV_MAX_Q || batch < 1 || heads < 1 || heads > MLAV_MAX_HEADS) return MLAV_ERR_SHAPE;
@@ -1644,6 +1887,8 @@ int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t
   if (opt && opt->nsplit > 0) {
     chunk = (max_kv + opt->nsplit - 1) / opt->nsplit;
     chunk = (chunk + kChunkGran - 1) / kChunkGran * kChunkGran;
+  } else if (batch > 1) {
+    chunk = batched_chunk(row_blocks(q, heads), batch, total_kv, max_kv, num_cus);
   } else {
     // one resident workgroup per CU: aim for about num_cus workgroups in total
     int64_t s_avg = num_cus / blocks;
@@ -1660,7 +1905,9 @@ int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t
   p->tile = kTile;
   p->chunk = chunk;
   const int kernel = opt ? opt->kernel : 0;
-  if (kernel == 0) {
+  if (kernel == 0 && chunk_list(batch, total_kv, max_kv)) {
+    p->grid = (int32_t)list_grid(row_blocks(q, heads), batch, total_kv, chunk, ns);
+  } else if (kernel == 0) {
     const int64_t per_xcd = (nwork + kXcds - 1) / kXcds;
     p->grid = (int32_t)(per_xcd * kXcds);
   } else {
@@ -1734,6 +1981,7 @@ int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* 
   a.per_xcd = (a.nwork + kXcds - 1) / kXcds;
   a.fixed_ns = 0;
   const int kernel = opt ? opt->kernel : 0;
+  a.list_run = kernel == 0 && chunk_list(a.batch, a.total_kv, a.max_kv) ? list_run(a.nrb) : 0;
   const int pv_mode = opt ? opt->pv_mode : 0;
   const bool compact = a.part_q != nullptr;
   const int phase = opt ? opt->phase : 0;

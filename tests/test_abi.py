@@ -279,3 +279,32 @@ def test_probe_library_exports_its_header():
     assert probe.mlav_probe_mfma(1, 10, None, buf, None) == 2
     assert probe.mlav_probe_mfma(1, 10, buf, None, None) == 2
     assert probe.mlav_probe_mfma_per_wave() == 16
+
+
+@pytest.mark.parametrize("lens,q,heads,cus", [
+    ([3766, 1817, 19196, 18627, 2261, 3227, 10553, 1319], 33, 64, 256),  # a ragged batch of 8
+    ([265] * 4, 9, 64, 256), ([4105] * 32, 9, 64, 256), ([16393] * 4, 9, 64, 256),  # equal lengths
+    ([10, 100000], 9, 64, 256), ([70] * 63 + [5000], 2, 8, 256), ([64, 65, 127, 128, 129], 1, 1, 8),
+])
+def test_batched_plan_covers_the_chunk_list(lib, lens, q, heads, cus):
+    """Batched plans: the chunks of every sequence fit the grid (each chunk's
+    row blocks are one work item each), whatever the lengths behind the host's
+    total and maximum; equal lengths fill the CUs in no more tile steps than
+    one chunk per sequence would, and unequal ones spread over the CUs."""
+    total, mx, b = sum(lens), max(lens), len(lens)
+    pl = _lib.plan(q, heads, b, total, mx, cus)
+    assert pl.tile == 32 and pl.chunk % 32 == 0 and pl.chunk >= 64
+    assert pl.nsplit == math.ceil(mx / pl.chunk)
+    nrb = math.ceil(q * heads / 64)
+    chunks = sum(math.ceil(n / pl.chunk) for n in lens)
+    assert chunks <= math.ceil(total / pl.chunk) + b - 1  # the bound the grid is sized for
+    assert pl.grid >= chunks * nrb and pl.grid % 8 == 0
+    assert pl.grid <= (math.ceil(total / pl.chunk) + b - 1) * nrb + 64  # rounded up to whole rounds of runs
+    if len(set(lens)) == 1:
+        # equal lengths: no more rounds of workgroups over the CUs than one chunk per sequence would take
+        rounds = math.ceil(math.ceil(chunks * nrb / 8) / (cus // 8))
+        one = math.ceil(math.ceil(b * nrb / 8) / (cus // 8))
+        assert rounds * pl.chunk <= one * math.ceil(mx / 32) * 32
+    else:
+        # unequal lengths: the long sequences are cut so that at least half the CUs get work
+        assert chunks * nrb >= min(cus // 2, nrb * b)
