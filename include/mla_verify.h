@@ -197,10 +197,20 @@ int32_t mla_verify_noalloc(const void* q_nope_absorbed, const void* q_rope, cons
  * [kv_offsets[b], kv_offsets[b+1]) (its prefix then its q_len tree tokens).
  *   q_nope_absorbed [batch, q_len, num_heads, 512], q_rope [batch, q_len, num_heads, 64]
  *   kv_latent [total_kv, 512], k_rope [total_kv, 64], tree_parent [batch, q_len]
- *   kv_offsets [batch + 1] int64 DEVICE array, kv_offsets[0] = 0
+ *   kv_offsets [batch + 1] int64 DEVICE array, non-decreasing, kv_offsets[0] = 0
  *   total_kv = kv_offsets[batch], max_kv = max_b (kv_offsets[b+1] - kv_offsets[b]):
  *   host copies of two device facts, used for planning and bounds checks
  *   out [batch, q_len, num_heads, 512], lse [batch, q_len, num_heads]
+ * Scheduling: sequences of unequal lengths run through a list of their KV
+ * chunks that the split kernel builds from kv_offsets (full chunks first,
+ * then each sequence's shorter last chunk, longest first), so that the work
+ * spreads over the CUs whatever the mix of lengths; equal lengths keep one
+ * range of (sequence, split, row block) items per XCD. The grid covers the
+ * chunks of any offsets that meet the contract above. A sequence whose own
+ * bounds are inconsistent (start below 0, end past total_kv, length below
+ * q_len or above max_kv) gets NaN rows. If the offsets are not
+ * non-decreasing, the other sequences are exact as long as their chunks fit
+ * that grid; past it, their rows are unspecified (never out of bounds).
  */
 int32_t mla_verify_batched(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,
                            const void* k_rope, const int32_t* tree_parent,
