@@ -132,3 +132,14 @@ def test_paged_reference_max_restart():
         out, lse = run_paged(case, pg, **kw)
         ro, rl = oracle_paged(case, pg)
         assert_parity(out, lse, ro, rl, f"paged restart {kw}")
+
+
+@pytest.mark.parametrize("batch,q,lo,hi,heads,seed", [(3, 9, 20, 2500, 64, 41), (70, 2, 4, 300, 8, 42)])
+def test_paged_ragged_batch(batch, q, lo, hi, heads, seed):
+    """Ragged batches through the page table: the chunk list path of the paged
+    kernel, with one lane per sequence (3) and with groups of 64 (70)."""
+    case = gen.make_batched_case(batch, q, prefix_lo=lo, prefix_hi=hi, tree="random", num_heads=heads, seed=seed)
+    pg = gen.make_paged(case, seed=seed + 1, extra_rows=500)
+    out, lse = run_paged(case, pg)
+    ro, rl = oracle_paged(case, pg)
+    assert_parity(out, lse, ro, rl, f"paged batch {batch}")
