@@ -62,6 +62,8 @@ def oracle(case):
     (65, 3, 8, 400, 16, 4),      # one past: the grouped search
     (150, 2, 4, 300, 8, 5),      # three groups of sequences
     (12, 33, 30, 900, 8, 6),     # several row blocks per token group
+    (256, 1, 2, 60, 4, 12),      # four full groups, loaded at once
+    (300, 1, 2, 120, 4, 11),     # five groups of 64 sequences, one row block each
 ])
 def test_ragged_batches(batch, q, lo, hi, heads, seed):
     case = gen.make_batched_case(batch, q, prefix_lo=lo, prefix_hi=hi, tree="random", num_heads=heads, seed=seed)
