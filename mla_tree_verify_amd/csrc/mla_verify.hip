@@ -634,10 +634,14 @@ __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&
 // replayed graph (same epoch) starts from 0 each time.
 constexpr int kMaxFusedSplits = 4;
 constexpr int kCoherent = 16;  // buffer cache policy: sc1 (device scope)
+
+// Compact partials of one row block (64 rows x 512 int16 values, 64 KB) lie
+// pair-major: [32 pairs of 16 dims][64 rows][16 dims]. Byte offset of row h's
+// 32 bytes of pair p within the block.
+__device__ inline int compact_byte_off(int p, int h) { return (p * kRows + h) * 32; }
 template <int kNs>
 __device__ inline void merge_block(const Args& a, LDS_AS char* xs, int b, int rbk, int wave, int lane) {
   constexpr int ns = kNs;
-  constexpr int kR = kNs == 2 ? 16 : 8;  // rows per round of loads (all of a round in flight)
   unsigned long long* tk = a.tickets + (int64_t)b * a.nrb + rbk;
   const int rows_seq = a.q * a.heads;
   const int64_t out_row0 = (int64_t)b * rows_seq + rbk * kRows;  // first output row of the block
@@ -660,48 +664,60 @@ __device__ inline void merge_block(const Args& a, LDS_AS char* xs, int b, int rb
   }
   __syncthreads();
   if (*(const LDS_AS int*)xs == 0) return;
-  // wave w merges rows [16 w, 16 w + 16) of the block, 8 at a time with every
-  // load in flight; lane l owns dims [8 l, 8 l + 8), lane s < ns fetches split
-  // s's lse and scale
+  // wave w merges pairs [8 w, 8 w + 8) of the block for all 64 rows: lane
+  // (h & 31, half) takes row 32 rh + (lane & 31), dims 16 p + 8 half .. + 8,
+  // for the 16 (pair, row half) units of the wave, kR units per round of loads
+  // (all of a round in flight); each lane fetches its row's lse and scale of
+  // every split
   const int sstride = a.nrb * kRows;
   const int64_t row_base = ((int64_t)b * a.nsplit * a.nrb + rbk) * kRows;  // split 0, row 0 of the block
-  __amdgpu_buffer_rsrc_t rs[kNs];  // the block's 64 rows of each split
+  __amdgpu_buffer_rsrc_t rs[kNs];  // the block's 64 KB of each split
 #pragma unroll
   for (int sp = 0; sp < kNs; ++sp)
     rs[sp] = make_rsrc(a.part_q + (row_base + (int64_t)sp * sstride) * kDl, kRows * kDl * 2);
+  const int half = lane >> 5;
+  constexpr int kR = 4;
 #pragma unroll 1
-  for (int k0 = 0; k0 < 16; k0 += kR) {
+  for (int u0 = 0; u0 < 16; u0 += kR) {
     u32x4_t qv[kR][kNs];
-    float lzs[kR], scs[kR];
+    float lz[kR][kNs], sc[kR][kNs];
 #pragma unroll
     for (int k = 0; k < kR; ++k) {
-      const int h = 16 * wave + k0 + k;
-#pragma unroll
-      for (int sp = 0; sp < kNs; ++sp)
-        qv[k][sp] = __builtin_amdgcn_raw_buffer_load_b128(rs[sp], h * (kDl * 2) + 16 * lane, 0, kCoherent);
-      const int64_t rr = row_base + (int64_t)(lane < ns ? lane : 0) * sstride + h;
-      lzs[k] = __hip_atomic_load(a.part_lse + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      scs[k] = __hip_atomic_load(a.part_scale + rr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-#pragma unroll
-    for (int k = 0; k < kR; ++k) {
-      const int h = 16 * wave + k0 + k;
-      float lz[kNs], sc[kNs];
-      float M = -INFINITY;
+      const int pr = 8 * wave + ((u0 + k) >> 1);
+      const int h = 32 * ((u0 + k) & 1) + (lane & 31);
 #pragma unroll
       for (int sp = 0; sp < kNs; ++sp) {
-        lz[sp] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lzs[k]), sp));
-        sc[sp] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scs[k]), sp));
-        M = fmax3(M, lz[sp]);
+        qv[k][sp] = __builtin_amdgcn_raw_buffer_load_b128(rs[sp], compact_byte_off(pr, h) + 16 * half, 0, kCoherent);
+        // lse (half 0) or scale (half 1) of the row; the lane halves swap below
+        const int64_t rr = row_base + (int64_t)sp * sstride + h;
+        lz[k][sp] = __hip_atomic_load((half ? a.part_scale : a.part_lse) + rr, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
       }
+    }
+#pragma unroll
+    for (int k = 0; k < kR; ++k)
+#pragma unroll
+      for (int sp = 0; sp < kNs; ++sp) {
+        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lz[k][sp]), __float_as_uint(lz[k][sp]),
+                                                        false, false);
+        lz[k][sp] = __uint_as_float(x[0]);
+        sc[k][sp] = __uint_as_float(x[1]);
+      }
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const int pr = 8 * wave + ((u0 + k) >> 1);
+      const int h = 32 * ((u0 + k) & 1) + (lane & 31);
+      float M = -INFINITY;
+#pragma unroll
+      for (int sp = 0; sp < kNs; ++sp) M = fmax3(M, lz[k][sp]);
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       float wsum = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int sp = 0; sp < kNs; ++sp) {
-          const float w = __builtin_amdgcn_exp2f((lz[sp] - M) * kLog2e);  // 0 for a split that saw no key
+          const float w = __builtin_amdgcn_exp2f((lz[k][sp] - M) * kLog2e);  // 0 for a split that saw no key
           wsum += w;
-          const float f = w * sc[sp];
+          const float f = w * sc[k][sp];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int32_t v = (int32_t)qv[k][sp][e];
@@ -712,10 +728,10 @@ __device__ inline void merge_block(const Args& a, LDS_AS char* xs, int b, int rb
       }
       if (h < nvalid) {
         const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-        float* o = a.out + (out_row0 + h) * kDl + 8 * lane;
+        float* o = a.out + (out_row0 + h) * kDl + 16 * pr + 8 * half;
         *(f32x4_t*)o = (f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv;
         *(f32x4_t*)(o + 4) = (f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv;
-        if (lane == 0) a.lse[out_row0 + h] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+        if (pr == 0 && half == 0) a.lse[out_row0 + h] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
       }
     }
   }
@@ -1253,10 +1269,11 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     // + e], so the row max is an in-lane max, one lane-pair swap and one
     // exchange with the partner wave (the other 256 dims), and adjacent dims
     // sit in adjacent elements, which v_cvt_pknorm_i16_f32 packs pairwise.
-    // One lane-pair swap per two 8-byte pieces makes 16-byte chunks of 8
-    // dims (the lower lane takes g = 2 gp, the upper g = 2 gp + 1). Rows are
-    // staged in int16 (row h in ring slot h >> 5 at (h & 31) * 1024, 16-byte
-    // chunk j at 16 (j ^ (h & 31))) and leave as one 1 KB store per row.
+    // One lane-pair swap per two 8-byte pieces gives each lane 16 bytes (8
+    // dims) of its row, the two lanes of a row holding the two halves of one
+    // 16-dim pair. The block's values lie pair-major in the workspace
+    // ([32 pairs][64 rows][16 dims], 32 B per row and pair), so every store
+    // leaves straight from registers as 1 KB (32 rows x 32 B of one pair).
     float m = partner_max(acc_amax);
     *(LDS_AS float*)(xs + wave * 2048 + 1024 + lane * 4) = m;  // clear of the l_tot words read above
     __syncthreads();
@@ -1267,8 +1284,16 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
     auto q2 = [&](float x, float y) {
       return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(x * g, y * g));
     };
-    const int hs = lane & 31;  // head & 31
-    LDS_AS char* st = ring(hh) + hs * 1024;
+    // The partial rows leave with device-scope stores (sc1: written through
+    // the XCD's L2). A block merged in this kernel needs that (another
+    // workgroup, maybe on another XCD, reads the rows at once); for the
+    // combine kernel it is measured 1 us faster per call at q 9, H 64,
+    // prefix 16384 than write-back stores, whose dirty lines the release at
+    // the kernel's end must write back before the combine can start.
+    // Rows past q * heads (the padding of the last block) are not stored: no
+    // merge reads them for an output, and each row merges on its own.
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.part_q + prow * kDl, kRows * kDl * 2);
+    const bool store_row = head < nvalid;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
@@ -1279,32 +1304,15 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
         const uint32_t b1 = q2(acc[db][8 * gp + 6], acc[db][8 * gp + 7]);
         const auto x = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
         const auto y = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-        const int j = 32 * kDh + 4 * db + 2 * gp + half;
-        *(LDS_AS u32x4_t*)(st + 16 * (j ^ hs)) = (u32x4_t){x[0], y[0], x[1], y[1]};
+        const int pair = 16 * kDh + 2 * db + gp;  // dims [16 pair, 16 pair + 16)
+        if (store_row)
+          __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){x[0], y[0], x[1], y[1]}, prs,
+                                                 compact_byte_off(pair, head) + 16 * half, 0, kCoherent);
       }
     }
-    // The partial rows leave with device-scope stores (sc1: written through
-    // the XCD's L2). A block merged in this kernel needs that (another
-    // workgroup, maybe on another XCD, reads the rows at once); for the
-    // combine kernel it is measured 1 us faster per call at q 9, H 64,
-    // prefix 16384 than write-back stores, whose dirty lines the release at
-    // the kernel's end must write back before the combine can start.
     if (kDh == 0 && half == 0)
       __hip_atomic_store(a.part_scale + prow + head, m * inv * (1.f / 32767.f), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.part_q + prow * kDl, kRows * kDl * 2);
-    LDS_AS char* src = ring(wave >> 1);  // rows 16 wave .. 16 wave + 15 lie in slot wave >> 1
-    // Rows past q * heads (the padding of the last block) are not stored: no
-    // merge writes them, and each row merges on its own.
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int h = 16 * wave + k;
-      if (h < nvalid) {
-        const u32x4_t v = *(const LDS_AS u32x4_t*)(src + (h & 31) * 1024 + 16 * (lane ^ (h & 31)));
-        __builtin_amdgcn_raw_buffer_store_b128(v, prs, h * (kDl * 2) + 16 * lane, 0, kCoherent);
-      }
-    }
   } else {
     // Stage the accumulators through LDS so that each global store writes
     // two 512-byte row pieces instead of 32-byte pieces of 32 rows. Ring
@@ -1557,175 +1565,177 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int64_t rows)
   if (d4 == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
 
-// Combine of compact (int16 + scale) partials, up to 32 splits: one wave per
-// row, one row per workgroup (the rows spread over every CU; at short
-// prefixes this launch is latency-bound, and four-wave workgroups left half
-// the CUs idle); lane l owns dims [8 l, 8 l + 8), one 16-byte load per split, and all
-// loads of a row are in flight together (one memory round trip; kBatch loads
-// per lane, the plan's split count rounded up to a multiple of 4).
-// Lanes 0..31 fetch the lse and scale values, the max and weight sum come
-// from 32-lane reductions, and each split's weight * scale reaches all lanes
-// by readlane.
-template <int kBatch>
-__global__ __launch_bounds__(64) void combine_compact_kernel(Args a, int64_t rows) {
-  fetch_combine_args(a, rows);
-  const int64_t row = blockIdx.x;
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const int64_t rows_b = (int64_t)a.q * a.heads;   // output rows per sequence
-  const int64_t rows_pad = (int64_t)a.nrb * kRows;  // partial rows per (sequence, split)
-  const int b = (int)(row / rows_b);
-  const int64_t rb = row - (int64_t)b * rows_b;
-  int64_t row0, n;
-  if (!seq_bounds(a, b, row0, n)) {
-    const float nan = __builtin_nanf("");
-    *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){nan, nan, nan, nan};
-    *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){nan, nan, nan, nan};
-    if (lane == 0) a.lse[row] = nan;
-    return;
-  }
-  const int ns = (int)((n + a.chunk - 1) / a.chunk);
-  if (ns <= 1) return;  // the split kernel wrote this row directly
-  const int64_t base = (int64_t)b * a.nsplit * rows_pad + rb;  // partial row of split 0
-  const float* pl = a.part_lse + base;
-  const float* psc = a.part_scale + base;
-  const int16_t* pq = a.part_q + base * kDl + 8 * lane;
-  u32x4_t qv[kBatch];
-#pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int sk = k < ns ? k : ns - 1;  // past the end: reload the last (weight 0)
-    qv[k] = __builtin_nontemporal_load((const u32x4_t*)(pq + (int64_t)sk * rows_pad * kDl));
-  }
-  const bool mine = lane < ns;
-  const float lz = mine ? pl[(int64_t)lane * rows_pad] : -INFINITY;
-  const float sc = mine ? psc[(int64_t)lane * rows_pad] : 0.f;
-  const float M = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_max(lz))));
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-    const float w = mine ? __builtin_amdgcn_exp2f((lz - M) * kLog2e) : 0.f;
-    wsum = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_sum(w))));
-    const float f = w * sc;
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), k));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int32_t v = (int32_t)qv[k][e];
-        acc[2 * e] += fk * (float)((v << 16) >> 16);
-        acc[2 * e + 1] += fk * (float)(v >> 16);
-      }
-    }
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  // streaming stores: the rows are not read again by this GPU before the call ends
-  __builtin_nontemporal_store((f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv, (f32x4_t*)(a.out + row * kDl + 8 * lane));
-  __builtin_nontemporal_store((f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv,
-                              (f32x4_t*)(a.out + row * kDl + 8 * lane + 4));
-  if (lane == 0) a.lse[row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+// Combine of compact (int16 + scale) partials. A work unit is (sequence b,
+// row block t, 16-dim pair p, row half rh): 32 rows x 16 dims, whose 32-byte
+// pieces lie one after another in every split's pair-major block, so each
+// partial load of a wave reads 1 KB contiguous. Lane (i, half) takes row
+// 32 rh + i of the block and dims 16 p + 8 half .. + 8, fetches its row's
+// lse and scale of every split itself, and merges with a running max.
+struct CombineUnit {
+  int b, t, p, h, half;
+  int64_t row;    // output row (sequence b's row t * 64 + h)
+  bool valid;     // the row exists (rows past q * heads pad the last block)
+};
+
+__device__ inline CombineUnit combine_unit(const Args& a, int64_t unit, int lane) {
+  CombineUnit u;
+  const int rh = (int)(unit & 1);
+  u.p = (int)((unit >> 1) & 31);
+  const int64_t bt = unit >> 6;
+  u.b = (int)(bt / a.nrb);
+  u.t = (int)(bt - (int64_t)u.b * a.nrb);
+  u.h = 32 * rh + (lane & 31);
+  u.half = lane >> 5;
+  const int64_t rows_b = (int64_t)a.q * a.heads;
+  const int64_t r = (int64_t)u.t * kRows + u.h;
+  u.valid = r < rows_b;
+  u.row = (int64_t)u.b * rows_b + r;
+  return u;
 }
 
-// Combine of compact (int16 + scale) partials for more than 32 splits: one
-// workgroup per row; wave w merges splits [w ns / 4, (w + 1) ns / 4) and the
-// four partial merges meet in LDS. Lane l owns dims [8 l, 8 l + 8), one 16-byte load per split. A
-// wave takes its splits in batches of kBatch (its share of the plan's splits
-// rounded up to a multiple of 4, at most 32; one memory round trip each): every
-// partial load of a batch is issued first, lanes 0..31 fetch the batch's lse
-// and scale values, the batch max and weight sum come from 32-lane
-// reductions, each split's weight * scale reaches all lanes by readlane, and
-// batches are merged with a running max, as in the fp32 combine.
+// NaN rows of a sequence with inconsistent offsets (this lane's 8 dims).
+__device__ inline void combine_nan(const Args& a, const CombineUnit& u) {
+  if (!u.valid) return;
+  const float nan = __builtin_nanf("");
+  float* o = a.out + u.row * kDl + 16 * u.p + 8 * u.half;
+  *(f32x4_t*)o = (f32x4_t){nan, nan, nan, nan};
+  *(f32x4_t*)(o + 4) = (f32x4_t){nan, nan, nan, nan};
+  if (u.p == 0 && u.half == 0) a.lse[u.row] = nan;
+}
+
+// Merges splits [s_lo, s_hi) of the unit's lane into (M, wsum, acc), kBatch
+// splits per memory round trip (every load of a batch issued first; entries
+// past s_hi reload the last split and get weight 0); batches meet through a
+// running max.
 template <int kBatch>
-__global__ __launch_bounds__(kThreads) void combine_compact_wide_kernel(Args a, int64_t rows) {
-  fetch_combine_args(a, rows);
-  __shared__ float x_acc[4][kDl];
-  __shared__ float x_m[4], x_w[4];
-  const int64_t row = blockIdx.x;
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int64_t rows_b = (int64_t)a.q * a.heads;   // output rows per sequence
-  const int64_t rows_pad = (int64_t)a.nrb * kRows;  // partial rows per (sequence, split)
-  const int b = (int)(row / rows_b);
-  const int64_t rb = row - (int64_t)b * rows_b;
-  int64_t row0, n;
-  if (!seq_bounds(a, b, row0, n)) {
-    if (wave == 0) {
-      const float nan = __builtin_nanf("");
-      *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){nan, nan, nan, nan};
-      *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){nan, nan, nan, nan};
-      if (lane == 0) a.lse[row] = nan;
-    }
-    return;
-  }
-  const int ns = (int)((n + a.chunk - 1) / a.chunk);
-  if (ns <= 1) return;  // the split kernel wrote this row directly
-  const int64_t base = (int64_t)b * a.nsplit * rows_pad + rb;  // partial row of split 0
-  const float* pl = a.part_lse + base;
-  const float* psc = a.part_scale + base;
-  const int16_t* pq = a.part_q + base * kDl + 8 * lane;
-  const int s_lo = wave * ns / 4, s_hi = (wave + 1) * ns / 4;
-  float M = -INFINITY, wsum = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+__device__ inline void combine_splits(const Args& a, const CombineUnit& u, int s_lo, int s_hi, float& M,
+                                      float& wsum, float (&acc)[8]) {
+  const int64_t sstride = (int64_t)a.nrb * kRows;                         // partial rows between splits
+  const int64_t prow0 = ((int64_t)u.b * a.nsplit * a.nrb + u.t) * kRows;  // split 0's block
+  const int16_t* pq = a.part_q + prow0 * kDl + compact_byte_off(u.p, u.h) / 2 + 8 * u.half;
+  // the row's lse (lanes of half 0) or scale (half 1): one load per split,
+  // and a swap of the two lane halves gives every lane both
+  const float* pv = (u.half ? a.part_scale : a.part_lse) + prow0 + u.h;
   for (int s0 = s_lo; s0 < s_hi; s0 += kBatch) {
     u32x4_t qv[kBatch];
+    float vv[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int sk = s0 + k < s_hi ? s0 + k : s_hi - 1;  // past the end: reload the last (weight 0)
-      qv[k] = __builtin_nontemporal_load((const u32x4_t*)(pq + (int64_t)sk * rows_pad * kDl));
+      const int sk = s0 + k < s_hi ? s0 + k : s_hi - 1;
+      qv[k] = __builtin_nontemporal_load((const u32x4_t*)(pq + (int64_t)sk * sstride * kDl));
+      vv[k] = pv[(int64_t)sk * sstride];
     }
-    const int sl = s0 + (lane & 31);
-    const bool mine = lane < kBatch && sl < s_hi;
-    const float lz = mine ? pl[(int64_t)sl * rows_pad] : -INFINITY;
-    const float sc = mine ? psc[(int64_t)sl * rows_pad] : 0.f;
-    const float bmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_max(lz))));
-    if (bmax == -INFINITY) continue;  // every split of this batch is empty (uniform)
-    const float m_new = fmax3(M, bmax);
+    float lz[kBatch], sc[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(vv[k]), __float_as_uint(vv[k]), false, false);
+      lz[k] = __uint_as_float(x[0]);
+      sc[k] = __uint_as_float(x[1]);
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mb = fmax3(mb, lz[k]);  // reloaded entries repeat a real one
+    if (mb == -INFINITY) continue;  // every split of this batch is empty for this row
+    const float m_new = fmax3(M, mb);
     const float r = __builtin_amdgcn_exp2f((M - m_new) * kLog2e);  // 0 while M = -inf
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= r;
     wsum *= r;
     M = m_new;
-    const float w = mine ? __builtin_amdgcn_exp2f((lz - M) * kLog2e) : 0.f;
-    wsum += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(half32_sum(w))));
-    const float f = w * sc;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const float fk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), k));
+      const float w = s0 + k < s_hi ? __builtin_amdgcn_exp2f((lz[k] - M) * kLog2e) : 0.f;
+      wsum += w;
+      const float f = w * sc[k];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int32_t v = (int32_t)qv[k][e];
-        acc[2 * e] += fk * (float)((v << 16) >> 16);
-        acc[2 * e + 1] += fk * (float)(v >> 16);
+        acc[2 * e] += f * (float)((v << 16) >> 16);
+        acc[2 * e + 1] += f * (float)(v >> 16);
       }
     }
   }
-  // merge the four waves' (M, wsum, acc) in LDS
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x_acc[wave][8 * lane + e] = acc[e];
-  if (lane == 0) {
-    x_m[wave] = M;
-    x_w[wave] = wsum;
+}
+
+__device__ inline void combine_store(const Args& a, const CombineUnit& u, float M, float wsum,
+                                     const float (&acc)[8]) {
+  if (!u.valid) return;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  float* o = a.out + u.row * kDl + 16 * u.p + 8 * u.half;
+  // streaming stores: the rows are not read again by this GPU before the call ends
+  __builtin_nontemporal_store((f32x4_t){acc[0], acc[1], acc[2], acc[3]} * inv, (f32x4_t*)o);
+  __builtin_nontemporal_store((f32x4_t){acc[4], acc[5], acc[6], acc[7]} * inv, (f32x4_t*)(o + 4));
+  if (u.p == 0 && u.half == 0) a.lse[u.row] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+}
+
+// Up to 32 splits: one wave per unit, all of a row's loads in one round
+// trip (kBatch loads per lane, the plan's split count rounded up to a
+// multiple of 4).
+template <int kBatch>
+__global__ __launch_bounds__(64) void combine_compact_kernel(Args a, int64_t units) {
+  fetch_combine_args(a, units);
+  const int64_t unit = blockIdx.x;
+  if (unit >= units) return;
+  const CombineUnit u = combine_unit(a, unit, threadIdx.x & 63);
+  int64_t row0, n;
+  if (!seq_bounds(a, u.b, row0, n)) {
+    combine_nan(a, u);
+    return;
   }
+  const int ns = (int)((n + a.chunk - 1) / a.chunk);
+  if (ns <= 1) return;  // the split kernel wrote this row directly
+  float M = -INFINITY, wsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  combine_splits<kBatch>(a, u, 0, ns, M, wsum, acc);
+  combine_store(a, u, M, wsum, acc);
+}
+
+// More than 32 splits: four waves per unit; wave w merges splits
+// [w ns / 4, (w + 1) ns / 4) in batches of kBatch (its share of the plan's
+// splits rounded up to a multiple of 4, at most 32), and the four partial
+// merges meet in LDS.
+template <int kBatch>
+__global__ __launch_bounds__(kThreads) void combine_compact_wide_kernel(Args a, int64_t units) {
+  fetch_combine_args(a, units);
+  __shared__ float x_acc[4][8][64];
+  __shared__ float x_m[4][64], x_w[4][64];
+  const int64_t unit = blockIdx.x;
+  if (unit >= units) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const CombineUnit u = combine_unit(a, unit, lane);
+  int64_t row0, n;
+  if (!seq_bounds(a, u.b, row0, n)) {
+    if (wave == 0) combine_nan(a, u);
+    return;
+  }
+  const int ns = (int)((n + a.chunk - 1) / a.chunk);
+  if (ns <= 1) return;  // the split kernel wrote this row directly
+  float M = -INFINITY, wsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int s_lo = wave * ns / 4, s_hi = (wave + 1) * ns / 4;
+  if (s_lo < s_hi) combine_splits<kBatch>(a, u, s_lo, s_hi, M, wsum, acc);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x_acc[wave][e][lane] = acc[e];
+  x_m[wave][lane] = M;
+  x_w[wave][lane] = wsum;
   __syncthreads();
   if (wave != 0) return;
   float mm = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) mm = fmax3(mm, x_m[w]);
+  for (int w = 0; w < 4; ++w) mm = fmax3(mm, x_m[w][lane]);
   float tot = 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (mm != -INFINITY) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float r = __builtin_amdgcn_exp2f((x_m[w] - mm) * kLog2e);  // 0 for a wave with nothing
-      tot += r * x_w[w];
+      const float r = __builtin_amdgcn_exp2f((x_m[w][lane] - mm) * kLog2e);  // 0 for a wave with nothing
+      tot += r * x_w[w][lane];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] += r * x_acc[w][8 * lane + e];
+      for (int e = 0; e < 8; ++e) o[e] += r * x_acc[w][e][lane];
     }
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  *(f32x4_t*)(a.out + row * kDl + 8 * lane) = (f32x4_t){o[0], o[1], o[2], o[3]} * inv;
-  *(f32x4_t*)(a.out + row * kDl + 8 * lane + 4) = (f32x4_t){o[4], o[5], o[6], o[7]} * inv;
-  if (lane == 0) a.lse[row] = tot > 0.f ? mm + __builtin_amdgcn_logf(tot) * kLn2 : -INFINITY;
+  combine_store(a, u, mm, tot, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -2010,6 +2020,8 @@ int launch(const Args& base, const mlav_plan& p, const mlav_options* opt, void* 
 merge:
   if (p.combine == 1) {
     const int64_t rows = (int64_t)a.batch * a.q * a.heads;
+    // compact partials: one unit per (sequence, row block, 16-dim pair, row half)
+    const int64_t units = (int64_t)a.batch * a.nrb * 64;
     if (compact) {
       if (p.nsplit <= 32) {
         // loads per lane: the plan's split count rounded up to a multiple of 4
@@ -2018,7 +2030,7 @@ merge:
                                       combine_compact_kernel<12>, combine_compact_kernel<16>,
                                       combine_compact_kernel<20>, combine_compact_kernel<24>,
                                       combine_compact_kernel<28>, combine_compact_kernel<32>};
-        hipLaunchKernelGGL(by_batch[(p.nsplit + 3) / 4 - 1], dim3((unsigned)rows), dim3(64), 0, st, a, rows);
+        hipLaunchKernelGGL(by_batch[(p.nsplit + 3) / 4 - 1], dim3((unsigned)units), dim3(64), 0, st, a, units);
       } else {
         // loads per lane and batch: a wave's share of the splits, rounded up to a multiple of 4
         using C = void (*)(Args, int64_t);
@@ -2026,8 +2038,8 @@ merge:
                                       combine_compact_wide_kernel<20>, combine_compact_wide_kernel<24>,
                                       combine_compact_wide_kernel<28>, combine_compact_wide_kernel<32>};
         const int per_wave = (p.nsplit + 3) / 4;  // at least 9 here
-        hipLaunchKernelGGL(by_batch[per_wave > 32 ? 5 : (per_wave + 3) / 4 - 3], dim3((unsigned)rows),
-                           dim3(kThreads), 0, st, a, rows);
+        hipLaunchKernelGGL(by_batch[per_wave > 32 ? 5 : (per_wave + 3) / 4 - 3], dim3((unsigned)units),
+                           dim3(kThreads), 0, st, a, units);
       }
     } else {
       hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(kThreads), 0, st, a, rows);
