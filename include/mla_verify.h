@@ -262,6 +262,11 @@ size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch
    Decisive Microbench", section "The KV-Split Solution": partitioning the KV
    across blocks so that enough blocks exist to keep every SM busy; page "The
    Validation Milestone", section "The Problem: Occupancy Starvation").
+   One sequence: about num_cus work items. A batch of equal lengths (total_kv
+   = batch x max_kv): the split count whose items fill the CUs in the fewest
+   tile steps. Unequal lengths: about two items per CU over the batch (a
+   fixed-cost estimate below 256 keys per chunk); plan_out->grid then covers
+   the kernel's list of every sequence's chunks (mla_verify_batched).
    Returns MLAV_ERR_SHAPE for sizes out of range, MLAV_ERR_ARG for
    num_cus < 1 or invalid options; plan_out is written only on MLAV_OK. */
 int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
