@@ -450,7 +450,7 @@ __device__ inline bool decode_list(const Args& a, int& b, int& s, int& t, int64_
     } else {
       const bool mine = sec == 0 ? (g0 + lane < B && !lok) : (lcls >= 0);
       const uint64_t m = __ballot(mine);
-      if (rank < __popcll(m)) {
+      if (rank < (int)__popcll(m)) {
         const int L = __builtin_ctzll(__ballot(mine && mask_rank(m) == rank));
         take(g0, L, sec == 0 ? 0 : readlane_i(lf, L), sec != 0);
         return true;
@@ -1020,10 +1020,7 @@ __device__ inline void split_body(const Args& a, LDS_AS char* r0, LDS_AS char* r
                     LDS_AS char* nbuf, int i, uint32_t vis) {
       constexpr bool kMasked = decltype(masked_tag)::value;
       const int dma_rel = tile_rel(i + 3);
-      auto kread = [&](int ks) {
-        const int cc = 36 * kDh + 2 * ks;  // even chunk of the 576-d row
-        return lds_b128(kbuf + k_frag_off<kDh>(kb, ks));
-      };
+      auto kread = [&](int ks) { return lds_b128(kbuf + k_frag_off<kDh>(kb, ks)); };
       // fragment order: the wave's own key step first (its weights are ready
       // first), then the partner's
       auto frag = [&](int nn) { return nn < 8 ? 8 * kDh + nn : 8 * (1 - kDh) + (nn - 8); };
