@@ -267,7 +267,8 @@ size_t mla_verify_workspace_size(int32_t q_len, int32_t num_heads, int32_t batch
    tile steps. Unequal lengths: about two items per CU over the batch (a
    fixed-cost estimate below 256 keys per chunk); plan_out->grid then covers
    the kernel's list of every sequence's chunks (mla_verify_batched).
-   Returns MLAV_ERR_SHAPE for sizes out of range, MLAV_ERR_ARG for
+   Returns MLAV_ERR_SHAPE for sizes out of range (also for a plan whose
+   split or combine launch would exceed 2^32 - 1 threads), MLAV_ERR_ARG for
    num_cus < 1 or invalid options; plan_out is written only on MLAV_OK. */
 int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t total_kv,
                         int64_t max_kv, int32_t num_cus, const mlav_options* opt,
@@ -289,7 +290,8 @@ int32_t mla_verify_plan(int32_t q_len, int32_t num_heads, int32_t batch, int64_t
  * (e.g. KV shards) can be stacked and combined the same way; a split that sees
  * no visible key has lse = -inf and a zero output. The plan must satisfy
  * nsplit = ceil((prefix_len + q_len) / chunk) with chunk a positive multiple of
- * plan->tile (32) and at most MLAV_MAX_KV; otherwise MLAV_ERR_ARG. Other
+ * plan->tile (32) and at most MLAV_MAX_KV; otherwise MLAV_ERR_ARG. A plan
+ * whose split launch would exceed 2^32 - 1 threads gives MLAV_ERR_SHAPE. Other
  * arguments as for mla_verify.
  */
 int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, const void* kv_latent,

@@ -1881,6 +1881,26 @@ int64_t list_grid(int64_t nrb, int32_t batch, int64_t total_kv, int64_t chunk, i
   return (runs + kXcds - 1) / kXcds * kXcds * run;
 }
 
+// One launch covers at most 2^32 - 1 work items (the dispatch packet's grid
+// size is 32 bits): larger plans are refused before anything is launched.
+constexpr int64_t kMaxLaunchItems = 0xffffffffll;
+
+// Workgroups of the split phase for `nwork` (sequence, row block, split)
+// items: the MFMA kernel rounds up to whole XCD rounds, the VALU kernel takes
+// 16 workgroups per item.
+int64_t split_grid(int kernel, int64_t nwork) {
+  return kernel == 0 ? (nwork + kXcds - 1) / kXcds * kXcds : nwork * 16;
+}
+
+// Work items of the combine launch (launch() below): int16 partials take one
+// 64-thread unit per (sequence, row block, 16-dim pair, row half), or one
+// 256-thread workgroup per unit beyond 32 splits; fp32 partials take a
+// 256-thread workgroup per two rows.
+int64_t combine_items(int64_t batch, int64_t nrb, int64_t rows, int64_t nsplit, bool compact) {
+  if (compact) return batch * nrb * 64 * (nsplit <= 32 ? 64 : kThreads);
+  return (rows + 1) / 2 * kThreads;
+}
+
 int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t max_kv,
               int32_t num_cus, const mlav_options* opt, mlav_plan* p) {
   if (q < 1 || q > MLAV_MAX_Q || batch < 1 || heads < 1 || heads > MLAV_MAX_HEADS) return MLAV_ERR_SHAPE;
@@ -1908,22 +1928,23 @@ int plan_impl(int32_t q, int32_t heads, int32_t batch, int64_t total_kv, int64_t
   const int64_t ns = (max_kv + chunk - 1) / chunk;
   const int64_t nwork = blocks * ns;
   if (nwork > (int64_t(1) << 30)) return MLAV_ERR_SHAPE;
-  p->nsplit = (int32_t)ns;
-  p->tile = kTile;
-  p->chunk = chunk;
   const int kernel = opt ? opt->kernel : 0;
-  if (kernel == 0 && chunk_list(batch, total_kv, max_kv)) {
-    p->grid = (int32_t)list_grid(row_blocks(q, heads), batch, total_kv, chunk, ns);
-  } else if (kernel == 0) {
-    const int64_t per_xcd = (nwork + kXcds - 1) / kXcds;
-    p->grid = (int32_t)(per_xcd * kXcds);
-  } else {
-    p->grid = (int32_t)(nwork * 16);
-  }
+  const int64_t grid = kernel == 0 && chunk_list(batch, total_kv, max_kv)
+                           ? list_grid(row_blocks(q, heads), batch, total_kv, chunk, ns)
+                           : split_grid(kernel, nwork);
   // merge = 1, 2..kMaxFusedSplits splits and int16 partials: the split kernel
   // merges them itself (one launch); otherwise the combine kernel runs
   const bool fused = ns >= 2 && ns <= kMaxFusedSplits && compact_partials(opt) && (opt ? opt->merge : 0) == 1;
-  p->combine = ns > 1 ? (fused ? 2 : 1) : 0;
+  const int combine = ns > 1 ? (fused ? 2 : 1) : 0;
+  if (grid * kThreads > kMaxLaunchItems) return MLAV_ERR_SHAPE;
+  if (combine == 1 && combine_items(batch, row_blocks(q, heads), (int64_t)batch * q * heads, ns,
+                                    compact_partials(opt)) > kMaxLaunchItems)
+    return MLAV_ERR_SHAPE;
+  p->nsplit = (int32_t)ns;
+  p->tile = kTile;
+  p->chunk = chunk;
+  p->grid = (int32_t)grid;
+  p->combine = combine;
   return MLAV_OK;
 }
 
@@ -2274,8 +2295,9 @@ int32_t mla_verify_partials(const void* q_nope_absorbed, const void* q_rope, con
     return MLAV_ERR_ARG;
   mlav_plan p = *plan;
   const int kernel = opt ? opt->kernel : 0;
-  const int64_t nwork = (int64_t)row_blocks(q_len, num_heads) * p.nsplit;
-  p.grid = kernel == 0 ? (int32_t)((nwork + kXcds - 1) / kXcds * kXcds) : (int32_t)(nwork * 16);
+  const int64_t grid = split_grid(kernel, (int64_t)row_blocks(q_len, num_heads) * p.nsplit);
+  if (grid * kThreads > kMaxLaunchItems) return MLAV_ERR_SHAPE;
+  p.grid = (int32_t)grid;
   p.combine = 0;
   Args a{};
   a.qn = (const uint16_t*)q_nope_absorbed;

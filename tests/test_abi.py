@@ -137,6 +137,26 @@ def test_plan_errors(lib):
     assert e.value.status == _lib.MLAV_ERR_ARG
 
 
+def test_plan_refuses_launches_beyond_32_bits(lib):
+    # 1024 row blocks x 16384 splits: 2^24 workgroups of 256 threads
+    n = 16384 * 32
+    with pytest.raises(_lib.MLAVError) as e:
+        _lib.plan(64, 1024, 1, n, n, 256, nsplit=16384)
+    assert e.value.status == _lib.MLAV_ERR_SHAPE
+    assert _lib.plan(64, 1024, 1, n, n, 256, nsplit=8192).nsplit == 8192
+    # 600 sequences of 64 x 1024 rows in two splits: the fp32-partial combine
+    # (128 threads per row) would pass 2^32 threads, the int16 one (64) does not
+    assert _lib.plan(64, 1024, 600, 600 * 128, 128, 256, nsplit=2).combine == 1
+    with pytest.raises(_lib.MLAVError) as e:
+        _lib.plan(64, 1024, 600, 600 * 128, 128, 256, nsplit=2, partials=1)
+    assert e.value.status == _lib.MLAV_ERR_SHAPE
+    # the VALU kernel takes 16 workgroups per item: 1024 row blocks x 2048 splits
+    assert _lib.plan(64, 1024, 1, 65536, 65536, 256, nsplit=2048).nsplit == 2048
+    with pytest.raises(_lib.MLAVError) as e:
+        _lib.plan(64, 1024, 1, 65536, 65536, 256, nsplit=2048, kernel=1)
+    assert e.value.status == _lib.MLAV_ERR_SHAPE
+
+
 # fake, aligned addresses: validation must reject the call before any use
 A = 0x10000
 
@@ -249,6 +269,10 @@ def test_partials_plan_chunk_bounds(lib):
     assert c(1, 48) == _lib.MLAV_ERR_ARG  # not a multiple of the tile
     assert c(0, 64) == _lib.MLAV_ERR_ARG
     assert c(3, 32, prefix=100) == _lib.MLAV_ERR_ARG  # 109 rows in chunks of 32 need 4 splits
+    # 1024 row blocks x 16384 chunks of 32 keys: 2^32 threads in the split launch
+    plan = _lib.Plan(16384, 32, 32, 0, 0)
+    assert f(A, A, A, A, A, 16384 * 32 - 64, 0.07, A, A, 64, 1024, ctypes.byref(plan), None,
+             ctypes.byref(opt)) == _lib.MLAV_ERR_SHAPE
 
 
 def test_combine_row_bound(lib):
