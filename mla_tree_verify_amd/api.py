@@ -33,6 +33,30 @@ def _check(t: torch.Tensor, name: str, dtype, shape, device) -> None:
         raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
+def _gpu_device(t: torch.Tensor, name: str, ndim: int, at_least: bool = False) -> torch.device:
+    """The device of `t`, which must be a GPU tensor with `ndim` dimensions (or
+    at least that many): the library dereferences every pointer on the GPU, where
+    a host pointer would fault."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("inputs must be on a GPU (the library has no CPU path)")
+    if t.dim() < ndim if at_least else t.dim() != ndim:
+        raise ValueError(f"{name} must have {'at least ' if at_least else ''}{ndim} dimensions, got {t.dim()}")
+    return t.device
+
+
+def _workspace(workspace: Optional[torch.Tensor], need: int, device) -> Tuple[Optional[int], int, Optional[torch.Tensor]]:
+    """(pointer, bytes, tensor) of the split workspace: the caller's, checked, or a new one."""
+    if workspace is None:
+        if need <= 0:
+            return None, 0, None
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+
+
 def _stream_ptr(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -49,9 +73,7 @@ def mla_verify(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tens
     phase: 0 = whole call, 1 = split kernel only, 2 = combine kernel only (same workspace).
     merge: 0 = the combine kernel merges the splits (default), 1 = plans of 2..4 splits
     merge in the split kernel (one launch)."""
-    if not q_nope.is_cuda:
-        raise ValueError("inputs must be on a GPU (the library has no CPU path)")
-    dev = q_nope.device
+    dev = _gpu_device(q_nope, "q_nope", 3)
     q, h = int(q_nope.shape[0]), int(q_nope.shape[1])
     n = int(prefix_len) + q
     _check(q_nope, "q_nope", torch.bfloat16, (q, h, DL), dev)
@@ -67,14 +89,12 @@ def mla_verify(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: torch.Tens
     _check(lse, "lse", torch.float32, (q, h), dev)
     lib = _lib.load()
     opt = _lib.options(nsplit, pv_mode, kernel, partials, phase, merge)
-    need = int(lib.mla_verify_workspace_size(q, h, 1, n, n, 0, ctypes.byref(opt)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.mla_verify_ex(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(), k_rope.data_ptr(),
-                           tree_parent.data_ptr(), int(prefix_len), float(scale), out.data_ptr(),
-                           lse.data_ptr(), q, h, ws_ptr, ws_bytes, _stream_ptr(dev), ctypes.byref(opt))
+    with torch.cuda.device(dev):  # the library plans for, and launches on, the current device
+        need = int(lib.mla_verify_workspace_size(q, h, 1, n, n, 0, ctypes.byref(opt)))
+        ws_ptr, ws_bytes, workspace = _workspace(workspace, need, dev)
+        rc = lib.mla_verify_ex(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(), k_rope.data_ptr(),
+                               tree_parent.data_ptr(), int(prefix_len), float(scale), out.data_ptr(),
+                               lse.data_ptr(), q, h, ws_ptr, ws_bytes, _stream_ptr(dev), ctypes.byref(opt))
     if rc != _lib.MLAV_OK:
         raise _lib.MLAVError(rc, "mla_verify")
     return out, lse
@@ -88,12 +108,11 @@ def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: to
                        kernel: int = 0, partials: int = 0, merge: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """B sequences: q_nope [B,q,H,512], kv rows of sequence b = [off[b], off[b+1]),
     tree_parent [B,q] int32, kv_offsets [B+1] int64 (CPU or device)."""
-    if not q_nope.is_cuda:
-        raise ValueError("inputs must be on a GPU (the library has no CPU path)")
-    dev = q_nope.device
+    dev = _gpu_device(q_nope, "q_nope", 4)
     bsz, q, h = int(q_nope.shape[0]), int(q_nope.shape[1]), int(q_nope.shape[2])
     total = int(kv_latent.shape[0])
-    if kv_offsets.dtype != torch.int64 or tuple(kv_offsets.shape) != (bsz + 1,):
+    if not isinstance(kv_offsets, torch.Tensor) or kv_offsets.dtype != torch.int64 or \
+            tuple(kv_offsets.shape) != (bsz + 1,):
         raise ValueError("kv_offsets must be int64 [B+1]")
     if max_kv is None or not kv_offsets.is_cuda:
         host = kv_offsets.detach().cpu()
@@ -110,17 +129,17 @@ def mla_verify_batched(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: to
         lse = torch.empty(bsz, q, h, dtype=torch.float32, device=dev)
     _check(out, "out", torch.float32, (bsz, q, h, DL), dev)
     _check(lse, "lse", torch.float32, (bsz, q, h), dev)
+    if not offs_dev.is_contiguous():
+        offs_dev = offs_dev.contiguous()
     lib = _lib.load()
     opt = _lib.options(nsplit, pv_mode, kernel, partials, merge=merge)
-    need = int(lib.mla_verify_workspace_size(q, h, bsz, total, max_kv, 0, ctypes.byref(opt)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.mla_verify_batched(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(), k_rope.data_ptr(),
-                                tree_parent.data_ptr(), offs_dev.data_ptr(), bsz, total, max_kv,
-                                float(scale), out.data_ptr(), lse.data_ptr(), q, h, ws_ptr, ws_bytes,
-                                _stream_ptr(dev), ctypes.byref(opt))
+    with torch.cuda.device(dev):  # the library plans for, and launches on, the current device
+        need = int(lib.mla_verify_workspace_size(q, h, bsz, total, max_kv, 0, ctypes.byref(opt)))
+        ws_ptr, ws_bytes, workspace = _workspace(workspace, need, dev)
+        rc = lib.mla_verify_batched(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(),
+                                    k_rope.data_ptr(), tree_parent.data_ptr(), offs_dev.data_ptr(), bsz, total,
+                                    max_kv, float(scale), out.data_ptr(), lse.data_ptr(), q, h, ws_ptr, ws_bytes,
+                                    _stream_ptr(dev), ctypes.byref(opt))
     if rc != _lib.MLAV_OK:
         raise _lib.MLAVError(rc, "mla_verify_batched")
     return out, lse
@@ -136,10 +155,8 @@ def mla_verify_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, pool_latent: to
     kv_index [N] int32 (logical row -> pool row). One sequence: q_nope [q,H,512],
     tree_parent [q], kv_offsets None (its N logical rows are its prefix then its
     tree). Batch: q_nope [B,q,H,512], tree_parent [B,q], kv_offsets [B+1] int64."""
-    if not q_nope.is_cuda:
-        raise ValueError("inputs must be on a GPU (the library has no CPU path)")
-    dev = q_nope.device
     batched = kv_offsets is not None
+    dev = _gpu_device(q_nope, "q_nope", 4 if batched else 3)
     if batched:
         bsz, q, h = int(q_nope.shape[0]), int(q_nope.shape[1]), int(q_nope.shape[2])
     else:
@@ -155,12 +172,13 @@ def mla_verify_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, pool_latent: to
     _check(tree_parent, "tree_parent", torch.int32, lead + (q,), dev)
     offs_ptr = None
     if batched:
-        if kv_offsets.dtype != torch.int64 or tuple(kv_offsets.shape) != (bsz + 1,):
+        if not isinstance(kv_offsets, torch.Tensor) or kv_offsets.dtype != torch.int64 or \
+                tuple(kv_offsets.shape) != (bsz + 1,):
             raise ValueError("kv_offsets must be int64 [B+1]")
         if max_kv is None:
             host = kv_offsets.detach().cpu()
             max_kv = int((host[1:] - host[:-1]).max().item())
-        kv_offsets = kv_offsets.to(dev) if not kv_offsets.is_cuda else kv_offsets
+        kv_offsets = kv_offsets.to(dev).contiguous()
         offs_ptr = kv_offsets.data_ptr()
     else:
         max_kv = total
@@ -172,15 +190,13 @@ def mla_verify_paged(q_nope: torch.Tensor, q_rope: torch.Tensor, pool_latent: to
     _check(lse, "lse", torch.float32, lead + (q, h), dev)
     lib = _lib.load()
     opt = _lib.options(nsplit, pv_mode, kernel, partials, merge=merge)
-    need = int(lib.mla_verify_workspace_size(q, h, bsz, total, int(max_kv), 0, ctypes.byref(opt)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.mla_verify_paged(q_nope.data_ptr(), q_rope.data_ptr(), pool_latent.data_ptr(), pool_rope.data_ptr(),
-                              kv_index.data_ptr(), pool, tree_parent.data_ptr(), offs_ptr, bsz, total,
-                              int(max_kv), float(scale), out.data_ptr(), lse.data_ptr(), q, h, ws_ptr, ws_bytes,
-                              _stream_ptr(dev), ctypes.byref(opt))
+    with torch.cuda.device(dev):  # the library plans for, and launches on, the current device
+        need = int(lib.mla_verify_workspace_size(q, h, bsz, total, int(max_kv), 0, ctypes.byref(opt)))
+        ws_ptr, ws_bytes, workspace = _workspace(workspace, need, dev)
+        rc = lib.mla_verify_paged(q_nope.data_ptr(), q_rope.data_ptr(), pool_latent.data_ptr(),
+                                  pool_rope.data_ptr(), kv_index.data_ptr(), pool, tree_parent.data_ptr(), offs_ptr,
+                                  bsz, total, int(max_kv), float(scale), out.data_ptr(), lse.data_ptr(), q, h,
+                                  ws_ptr, ws_bytes, _stream_ptr(dev), ctypes.byref(opt))
     if rc != _lib.MLAV_OK:
         raise _lib.MLAVError(rc, "mla_verify_paged")
     return out, lse
@@ -193,7 +209,7 @@ def mla_verify_partials(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: t
     """The split phase for `plan`: part_out [S, q, H, 512], part_lse [S, q, H] (fp32); when
     q * H is not a multiple of 64 the rows are padded: [S, R, 512] and [S, R] with R = q * H
     rounded up to a multiple of 64."""
-    dev = q_nope.device
+    dev = _gpu_device(q_nope, "q_nope", 3)
     q, h = int(q_nope.shape[0]), int(q_nope.shape[1])
     n = int(prefix_len) + q
     _check(q_nope, "q_nope", torch.bfloat16, (q, h, DL), dev)
@@ -212,10 +228,11 @@ def mla_verify_partials(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: t
     _check(part_out, "part_out", torch.float32, lead + (DL,), dev)
     _check(part_lse, "part_lse", torch.float32, lead, dev)
     opt = _lib.options(0, pv_mode, kernel)
-    rc = _lib.load().mla_verify_partials(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(),
-                                         k_rope.data_ptr(), tree_parent.data_ptr(), int(prefix_len),
-                                         float(scale), part_out.data_ptr(), part_lse.data_ptr(), q, h,
-                                         ctypes.byref(plan), _stream_ptr(dev), ctypes.byref(opt))
+    with torch.cuda.device(dev):
+        rc = _lib.load().mla_verify_partials(q_nope.data_ptr(), q_rope.data_ptr(), kv_latent.data_ptr(),
+                                             k_rope.data_ptr(), tree_parent.data_ptr(), int(prefix_len),
+                                             float(scale), part_out.data_ptr(), part_lse.data_ptr(), q, h,
+                                             ctypes.byref(plan), _stream_ptr(dev), ctypes.byref(opt))
     if rc != _lib.MLAV_OK:
         raise _lib.MLAVError(rc, "mla_verify_partials")
     return part_out, part_lse
@@ -224,7 +241,7 @@ def mla_verify_partials(q_nope: torch.Tensor, q_rope: torch.Tensor, kv_latent: t
 def combine(part_out: torch.Tensor, part_lse: torch.Tensor,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """LSE merge of caller-made partials: part_out [S, rows, 512], part_lse [S, rows]."""
-    dev = part_out.device
+    dev = _gpu_device(part_out, "part_out", 2, at_least=True)
     s = int(part_out.shape[0])
     part_out = part_out.reshape(s, -1, DL)
     part_lse = part_lse.reshape(s, -1)
@@ -235,8 +252,11 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor,
         out = torch.empty(rows, DL, dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(rows, dtype=torch.float32, device=dev)
-    rc = _lib.load().mla_verify_combine(part_out.data_ptr(), part_lse.data_ptr(), s, rows, out.data_ptr(),
-                                        lse.data_ptr(), _stream_ptr(dev))
+    _check(out, "out", torch.float32, (rows, DL), dev)
+    _check(lse, "lse", torch.float32, (rows,), dev)
+    with torch.cuda.device(dev):
+        rc = _lib.load().mla_verify_combine(part_out.data_ptr(), part_lse.data_ptr(), s, rows, out.data_ptr(),
+                                            lse.data_ptr(), _stream_ptr(dev))
     if rc != _lib.MLAV_OK:
         raise _lib.MLAVError(rc, "mla_verify_combine")
     return out, lse

@@ -295,6 +295,20 @@ def test_workspace_too_small_is_rejected():
     assert e.value.status == _lib.MLAV_ERR_WORKSPACE
 
 
+def test_workspace_off_the_device_is_rejected():
+    """A host or strided workspace never reaches the library (its pointer would
+    be dereferenced on the GPU)."""
+    case = gen.make_workload("q9_p4096")
+    d = dev_case(case)
+    args = (d["q_nope"], d["q_rope"], d["kv_latent"], d["k_rope"], d["tree_parent"], case.prefix_len, case.scale)
+    need = _lib.workspace_size(case.q_len, 64, 1, case.prefix_len + case.q_len, case.prefix_len + case.q_len)
+    assert need > 0
+    with pytest.raises(ValueError, match="workspace"):
+        api.mla_verify(*args, workspace=torch.empty(need, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="workspace"):
+        api.mla_verify(*args, workspace=torch.empty(2 * need, dtype=torch.uint8, device=DEV)[::2])
+
+
 def test_partials_then_combine_equals_full_call():
     case = gen.make_workload("q9_p16384")
     d = dev_case(case)
