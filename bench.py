@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-extra-configs", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA and copy peak measurements")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="print the measured MFMA and copy peaks as one JSON line and exit")
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
                     help="after timing, run one device copy of this size (counter calibration)")
     ap.add_argument("--pv-mode", type=int, default=0)
@@ -83,9 +85,12 @@ def source_digest() -> str:
 
 
 def read_counters(workload: str, paged: bool = False):
-    """HBM bytes per split-kernel launch and its MFMA-busy fraction from the
+    """HBM bytes per split-kernel launch and its MFMA-busy fractions from the
     committed counter summary, or (None, None) when there is none or the
-    kernel source changed since."""
+    kernel source changed since. The fractions: MFMA busy cycles over the SIMD
+    cycles of the CUs while they held a workgroup, and over all SIMDs in the
+    dispatch's GPU-active window (a lower bound: for a short dispatch that
+    window also holds the profiler's launch and drain)."""
     path = os.path.join(PROFILES, f"split_mfma_kernel_{workload}{'_paged' if paged else ''}_counters.txt")
     if not os.path.exists(path):
         return None, None
@@ -102,7 +107,8 @@ def read_counters(workload: str, paged: bool = False):
     except (KeyError, ValueError):
         traffic = None
     try:
-        busy = float(kv["mfma_busy_fraction"])
+        busy = {"on_occupied_cus": float(kv["mfma_busy_fraction"]),
+                "gpu_window_lower_bound": float(kv["mfma_busy_fraction_gpu_window"])}
     except (KeyError, ValueError):
         busy = None
     return traffic, busy
@@ -376,6 +382,9 @@ def main() -> int:
     num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
     _lib.load()
     peaks = {} if args.no_peaks else measured_peaks(torch, dev, num_cus)
+    if args.peaks_only:
+        print(json.dumps({"measured_peaks": peaks}))
+        return 0
 
     spec = gen.WORKLOADS[args.workload]
     H = args.heads
