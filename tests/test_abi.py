@@ -332,3 +332,27 @@ def test_batched_plan_covers_the_chunk_list(lib, lens, q, heads, cus):
     else:
         # unequal lengths: the long sequences are cut so that at least half the CUs get work
         assert chunks * nrb >= min(cus // 2, nrb * b)
+
+
+def test_plain_c_caller(tmp_path):
+    """tests/c_abi_check.c: the headers compile as strict C99, the library
+    links from C, and its host-only entry points behave as documented."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    libdir = os.path.join(ROOT, "mla_tree_verify_amd")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    for name in ("libmla_verify.so", "libmla_verify_probe.so"):
+        if not os.path.exists(os.path.join(libdir, name)):
+            pytest.skip(f"{name} not built")
+    exe = str(tmp_path / "c_abi_check")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c_abi_check.c"), "-L", libdir, "-lmla_verify", "-lmla_verify_probe",
+           f"-Wl,-rpath,{libdir}", "-o", exe]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    assert "c abi ok" in run.stdout
