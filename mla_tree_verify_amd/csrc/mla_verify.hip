@@ -38,9 +38,10 @@
 //  * Softmax weights enter the value product as a bf16 hi+lo pair (two MFMAs
 //    sharing the V operand), about 16 significant bits; a single bf16 weight
 //    is an option.
-//  * Workgroup ids are mapped so that all row blocks of one KV chunk run on
-//    the same XCD (ids are dealt round-robin over the 8 XCDs), and the chunk
-//    is read from HBM once into that XCD's L2.
+//  * Workgroup ids are mapped so that consecutive ids on one XCD (ids are
+//    dealt round-robin over the 8 XCDs) take the row blocks of one KV chunk,
+//    so a chunk is read from HBM into one XCD's L2 and reused there (a chunk
+//    whose row blocks straddle two XCDs is read by both).
 
 #include <hip/hip_runtime.h>
 
@@ -108,10 +109,11 @@ struct Args {
   int64_t pool_rows;     // paged KV: rows of the pool
   float* out;            // [B, q, H, 512]
   float* lse;            // [B, q, H]
-  float* part_o;         // [B, S, q, H, 512] fp32 partials
-  int16_t* part_q;       // [B, S, q, H, 512] compact partials (int16 x part_scale)
-  float* part_scale;     // [B, S, q, H]
-  float* part_lse;       // [B, S, q, H]
+  // split partials, over [B, S, nrb * 64] rows (each sequence's q * H rows padded to whole row blocks)
+  float* part_o;         // [B, S, nrb * 64, 512] fp32 partials
+  int16_t* part_q;       // [B, S, nrb] blocks of 64 KB: int16 x part_scale, pair-major (compact_byte_off)
+  float* part_scale;     // [B, S, nrb * 64]
+  float* part_lse;       // [B, S, nrb * 64]
   unsigned long long* tickets;  // merge in the split kernel: [B, nrb] (epoch << 16 | arrivals)
   unsigned long long epoch;     // this call's ticket epoch (48 bits, not 0)
   int64_t single_n;
@@ -595,7 +597,8 @@ __device__ inline int opaque(int x) {
 }
 
 // Partial scores of one tile over this wave's half of the 576 dims:
-// S^T[32 keys x 32 heads] = K[32 keys x 288] Q^T[288 x 32 heads].
+// S^T[32 keys x 32 rows] = K[32 keys x 288] Q^T[288 x 32 rows] (a row is one
+// (token, head) pair).
 template <int kDh>
 __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&qreg)[18],
                                        const KBases& kb) {
@@ -607,10 +610,10 @@ __device__ inline f32x16_t tile_scores(const LDS_AS char* buf, const bf16x8_t (&
   return sc;
 }
 
-// One workgroup = one draft token x 64 heads x one KV chunk; 4 waves =
-// 2 head halves (hh) x 2 dim halves (kDh). Both waves of a head half compute
-// partial scores of every tile over their dim half. The softmax is split
-// between them: the wave with dim half kDh owns the tile's keys
+// One workgroup = one row block (64 consecutive (token, head) rows) x one KV
+// chunk; 4 waves = 2 row halves (hh) x 2 dim halves (kDh). Both waves of a
+// row half compute partial scores of every tile over their dim half. The
+// softmax is split between them: the wave with dim half kDh owns the tile's keys
 // [16 kDh, 16 kDh + 16) (accumulator elements r = 8 kDh .. 8 kDh + 7), so
 // each wave sends its partner the partial scores of the partner's keys,
 // turns the full scores of its own keys into bf16 hi + lo weights, and the
