@@ -318,6 +318,29 @@ def measured_peaks(torch, dev, num_cus: int) -> dict:
         res["mfma_cycles_per_instruction"] = round(cycles / (iters * per_wave), 2)
         res["mfma_probe"] = (f"{grid} workgroups x 4 waves (one per SIMD), {iters * per_wave} independent "
                              "v_mfma_f32_32x32x16_bf16 per wave over 8 accumulators")
+        # the split kernel's loop step as a bare data flow: cycles per step with
+        # each part added to its 50 MFMAs per wave (1600 cycles at 32 per MFMA)
+        probe.mlav_probe_step_mix.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        probe.mlav_probe_step_mix.restype = ctypes.c_int32
+        probe.mlav_probe_steps_per_iteration.restype = ctypes.c_int32
+        src = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)  # MLAV_MIX_SRC_BYTES
+        mix_iters = 250
+        steps = mix_iters * probe.mlav_probe_steps_per_iteration()
+        mix = {}
+        for name, parts in (("mfma", 0), ("mfma+lds", 1), ("mfma+dma", 2), ("mfma+lds+dma", 3),
+                            ("mfma+lds+dma+barriers", 7)):
+            for _ in range(2):
+                if probe.mlav_probe_step_mix(grid, mix_iters, parts, src.data_ptr(), out.data_ptr(), cyc.data_ptr(),
+                                             stream.cuda_stream) != 0:
+                    raise RuntimeError("step-mix probe launch failed")
+            torch.cuda.synchronize()
+            mix[name] = round(float(cyc.double().mean().item()) / steps, 1)
+        res["step_mix_cycles"] = mix
+        res["step_mix_probe"] = ("the split kernel's loop step without its data dependencies, cycles per 32-key "
+                                 "step: 50 MFMAs per wave, plus its LDS operand reads (136 KB per CU), its nine 1 KB "
+                                 "direct-to-LDS tile loads per wave and its two barriers")
+        del src
     nb = 1 << 30
     src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)

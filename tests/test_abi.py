@@ -282,14 +282,15 @@ def test_combine_row_bound(lib):
 
 
 def test_probe_library_exports_its_header():
-    """The benchmark's MFMA peak probe: a separate library with its own header."""
+    """The benchmark's probes: a separate library with its own header."""
     path = os.path.join(ROOT, "mla_tree_verify_amd", "libmla_verify_probe.so")
     if not os.path.exists(path):
         pytest.skip("probe library not built")
     text = open(os.path.join(ROOT, "include", "mla_verify_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     declared = sorted(set(re.findall(r"\b(mlav_probe\w*)\s*\(", text)))
-    assert declared == ["mlav_probe_mfma", "mlav_probe_mfma_per_wave"]
+    assert declared == ["mlav_probe_mfma", "mlav_probe_mfma_per_wave", "mlav_probe_step_mix",
+                        "mlav_probe_steps_per_iteration"]
     probe = ctypes.CDLL(path)
     for name in declared:
         assert hasattr(probe, name)
@@ -303,6 +304,14 @@ def test_probe_library_exports_its_header():
     assert probe.mlav_probe_mfma(1, 10, None, buf, None) == 2
     assert probe.mlav_probe_mfma(1, 10, buf, None, None) == 2
     assert probe.mlav_probe_mfma_per_wave() == 16
+    probe.mlav_probe_step_mix.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    probe.mlav_probe_step_mix.restype = ctypes.c_int32
+    assert probe.mlav_probe_step_mix(1, 10, 8, buf, buf, buf, None) == 2  # parts beyond the three bits
+    assert probe.mlav_probe_step_mix(1, 10, -1, buf, buf, buf, None) == 2
+    assert probe.mlav_probe_step_mix(0, 10, 7, buf, buf, buf, None) == 2
+    assert probe.mlav_probe_step_mix(1, 10, 7, None, buf, buf, None) == 2
+    assert probe.mlav_probe_steps_per_iteration() == 4
 
 
 @pytest.mark.parametrize("lens,q,heads,cus", [
