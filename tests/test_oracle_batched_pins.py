@@ -3,8 +3,8 @@
 The batched layout follows the ragged-prefix workload: sequence b owns KV rows
 [off[b], off[b+1]) of one array, its prefix followed by its q tree tokens, so
 its prefix length is off[b+1] - off[b] - q, and each sequence has its own tree
-(the survey's reading of the batched configuration; the pages benchmark one
-stream only, page "The Decisive Microbench", section "The Message").
+(this library's reading of the batched configuration; the pages benchmark
+one stream only, page "The Decisive Microbench", section "The Message").
 
   * a pure-Python brute force over the concatenated arrays, with the offsets
     and every ancestor walk written out by hand, on a 3-sequence ragged toy
