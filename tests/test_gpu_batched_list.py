@@ -64,6 +64,8 @@ def oracle(case):
     (12, 33, 30, 900, 8, 6),     # several row blocks per token group
     (256, 1, 2, 60, 4, 12),      # four full groups, loaded at once
     (300, 1, 2, 120, 4, 11),     # five groups of 64 sequences, one row block each
+    (1000, 2, 2, 200, 4, 21),    # sixteen groups
+    (4096, 1, 1, 16, 2, 23),     # 64 groups of short sequences, several rounds of workgroups per CU
 ])
 def test_ragged_batches(batch, q, lo, hi, heads, seed):
     case = gen.make_batched_case(batch, q, prefix_lo=lo, prefix_hi=hi, tree="random", num_heads=heads, seed=seed)
